@@ -1,0 +1,206 @@
+"""Python binding of libaqd, the MI355X additive-codebook decode kernels.
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in ``include/aqd.h``.  PyTorch provides device memory and
+the current stream.  The functions keep the C names; each takes torch CUDA
+tensors and returns the output tensor (allocated here unless ``out=`` is
+given).  If the library is not built, or a call fails, an exception is raised:
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libaqd.so")
+
+AQD_F16, AQD_BF16, AQD_F32, AQD_BF16X2 = 0, 1, 2, 3
+_TORCH_DT = {torch.float16: AQD_F16, torch.bfloat16: AQD_BF16, torch.float32: AQD_F32}
+
+
+class AqdError(RuntimeError):
+    """A libaqd call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class aqd_layer(ctypes.Structure):
+    _fields_ = [("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64), ("M", ctypes.c_int32),
+                ("group", ctypes.c_int32), ("code_bits", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_VP, _SZ, _I32, _I64, _INT = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
+_LP = ctypes.POINTER(aqd_layer)
+_SIGNATURES = {
+    "aqd_abi_version": (_INT, []),
+    "aqd_status_string": (ctypes.c_char_p, [_INT]),
+    "aqd_last_error": (ctypes.c_char_p, []),
+    "aqd_packed_codes_bytes": (_SZ, [_LP]),
+    "aqd_pack_codes": (_INT, [_VP, _VP, _LP, _VP]),
+    "aqd_unpack_codes": (_INT, [_VP, _VP, _LP, _VP]),
+    "aqd_hadamard_rotate": (_INT, [_VP, _VP, _INT, _INT, _I64, _I64, _I32, _VP]),
+    "aqd_gemv_workspace_bytes": (_SZ, [_LP, _I32]),
+    "aqd_gemv": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
+    "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
+    "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libaqd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m additive_codebook_gemv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def layer(d_out: int, d_in: int, M: int) -> aqd_layer:
+    return aqd_layer(d_out, d_in, M, 8, 8)
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise AqdError(status, f"{L.aqd_status_string(status).decode()}: {L.aqd_last_error().decode()}")
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libaqd must be contiguous")
+    return t.data_ptr() or None
+
+
+def aqd_packed_codes_bytes(d_out: int, d_in: int, M: int) -> int:
+    return int(lib().aqd_packed_codes_bytes(ctypes.byref(layer(d_out, d_in, M))))
+
+
+def aqd_pack_codes(codes: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """codes: uint8 [d_out][d_in/8][M] on the GPU -> packed uint8 tiles."""
+    d_out, G, M = codes.shape
+    L = layer(d_out, G * 8, M)
+    n = int(lib().aqd_packed_codes_bytes(ctypes.byref(L)))
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=codes.device)
+    _check(lib().aqd_pack_codes(_ptr(codes), _ptr(out), ctypes.byref(L), _stream()))
+    return out
+
+
+def aqd_unpack_codes(packed: torch.Tensor, d_out: int, d_in: int, M: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((d_out, d_in // 8, M), dtype=torch.uint8, device=packed.device)
+    L = layer(d_out, d_in, M)
+    _check(lib().aqd_unpack_codes(_ptr(packed), _ptr(out), ctypes.byref(L), _stream()))
+    return out
+
+
+def aqd_hadamard_rotate(x: torch.Tensor, block: int, out_dtype: int = AQD_F16,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x: [batch][d_in] fp16/bf16/fp32 -> rotated [batch][d_in] (or [2][batch][d_in] for AQD_BF16X2)."""
+    x2 = x.reshape(-1, x.shape[-1])
+    batch, d_in = x2.shape
+    if out is None:
+        if out_dtype == AQD_BF16X2:
+            out = torch.empty((2, batch, d_in), dtype=torch.bfloat16, device=x.device)
+        else:
+            tdt = {AQD_F16: torch.float16, AQD_BF16: torch.bfloat16, AQD_F32: torch.float32}[out_dtype]
+            out = torch.empty((batch, d_in), dtype=tdt, device=x.device)
+    _check(lib().aqd_hadamard_rotate(_ptr(x2), _ptr(out), _TORCH_DT[x.dtype], out_dtype, batch, d_in, block,
+                                     _stream()))
+    return out
+
+
+def aqd_gemv_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:
+    return int(lib().aqd_gemv_workspace_bytes(ctypes.byref(layer(d_out, d_in, M)), batch))
+
+
+def aqd_gemv(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, k: int, x_rot: torch.Tensor,
+             d_out: int, d_in: int, M: int, out: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[batch][d_out] fp16 = s * (W_k @ x_rot) for fp16 x_rot [batch][d_in], batch 1..8."""
+    x2 = x_rot if x_rot.dim() == 2 else x_rot.reshape(1, -1)
+    batch = x2.shape[0]
+    L = layer(d_out, d_in, M)
+    if out is None:
+        out = torch.empty((batch, d_out), dtype=torch.float16, device=x_rot.device)
+    need = int(lib().aqd_gemv_workspace_bytes(ctypes.byref(L), batch))
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
+    _check(lib().aqd_gemv(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x2), _ptr(out), batch,
+                          ctypes.byref(L), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                          _stream()))
+    return out
+
+
+def aqd_gemm_small_batch_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:
+    return int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(layer(d_out, d_in, M)), batch))
+
+
+def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, k: int,
+                         x_rot: torch.Tensor, d_out: int, d_in: int, M: int, x_dtype: int = AQD_BF16X2,
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[batch][d_out] fp32 for x_rot bf16 [batch][d_in] (AQD_BF16) or [2][batch][d_in] (AQD_BF16X2)."""
+    batch = x_rot.shape[-2]
+    L = layer(d_out, d_in, M)
+    if out is None:
+        out = torch.empty((batch, d_out), dtype=torch.float32, device=x_rot.device)
+    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch))
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
+    _check(lib().aqd_gemm_small_batch(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x_rot), x_dtype,
+                                      _ptr(out), batch, ctypes.byref(L), _ptr(workspace),
+                                      workspace.numel() if workspace is not None else 0, _stream()))
+    return out
+
+
+class QuantizedLinear:
+    """One additive-codebook linear resident on the GPU: packed codes, codebooks, scales.
+
+    ``forward(x, k)`` rotates the activation online and applies the k-codebook
+    product: batch 1..8 through the GEMV, larger batches through the bf16
+    matrix-core path (fp32 output).
+    """
+
+    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, block: int):
+        d_out, G, M = codes.shape
+        self.d_out, self.d_in, self.M, self.block = d_out, G * 8, M, block
+        self.packed = aqd_pack_codes(codes)
+        self.codebooks = codebooks.contiguous()
+        self.scales = scales.contiguous()
+        self.workspace = None
+        n = max(aqd_gemv_workspace_bytes(d_out, self.d_in, M, 8),
+                aqd_gemm_small_batch_workspace_bytes(d_out, self.d_in, M, 64))
+        if n:
+            self.workspace = torch.zeros(n, dtype=torch.uint8, device=codes.device)
+
+    def forward(self, x: torch.Tensor, k: int) -> torch.Tensor:
+        x2 = x.reshape(-1, self.d_in)
+        if x2.shape[0] <= 8:
+            xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
+            return aqd_gemv(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
+                            workspace=self.workspace)
+        xr = aqd_hadamard_rotate(x2, self.block, AQD_BF16X2)
+        return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
+                                    AQD_BF16X2, workspace=self.workspace)

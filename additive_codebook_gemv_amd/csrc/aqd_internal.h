@@ -1,0 +1,81 @@
+// Internal declarations shared by the HIP sources of libaqd (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+
+#include "aqd.h"
+
+namespace aqd {
+
+// Packed code tiles.  Plane-major: all tiles of codebook 0, then codebook 1, ...
+// Inside a plane, tiles are ordered [group tile jt][row tile it]; a tile covers
+// TILE_ROWS consecutive rows and TILE_GROUPS consecutive 8-wide groups and is
+// stored lane-major: byte (l * TILE_ROWS + r) holds the code of row
+// it*TILE_ROWS + r, group jt*TILE_GROUPS + l.  One tile is 1 KiB, so a wave of
+// 64 lanes loading 16 bytes each reads one whole tile, and lane l receives the
+// codes of one group for 16 consecutive rows.  Rows and groups past the layer
+// edge are padding (code 0) and never contribute.
+constexpr int TILE_ROWS = 16;
+constexpr int TILE_GROUPS = 64;
+constexpr int TILE_BYTES = TILE_ROWS * TILE_GROUPS;
+constexpr int GROUP = 8;
+constexpr int CODEWORDS = 256;
+constexpr int MAX_M = 8;
+
+struct Geometry {
+    int64_t d_out, d_in, G;        // G = d_in / 8
+    int64_t n_rt, n_gt;            // row tiles, group tiles
+    int64_t plane_bytes;           // n_rt * n_gt * TILE_BYTES
+    int32_t M;
+};
+
+inline Geometry geometry(const aqd_layer& L) {
+    Geometry g;
+    g.d_out = L.d_out;
+    g.d_in = L.d_in;
+    g.G = L.d_in / GROUP;
+    g.n_rt = (L.d_out + TILE_ROWS - 1) / TILE_ROWS;
+    g.n_gt = (g.G + TILE_GROUPS - 1) / TILE_GROUPS;
+    g.plane_bytes = g.n_rt * g.n_gt * TILE_BYTES;
+    g.M = L.M;
+    return g;
+}
+
+// Per-thread error text (set by the C entry points).
+void set_error(const std::string& s);
+
+// ---- launchers (return hipSuccess or the launch error) --------------------
+hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, const Geometry& g, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, uint8_t* codes, const Geometry& g, hipStream_t s);
+hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in,
+                           int block, hipStream_t s);
+size_t gemv_workspace_bytes(const Geometry& g, int batch);
+hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                       const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
+size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
+hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                          const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,
+                          hipStream_t s);
+
+// ---- device helpers --------------------------------------------------------
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
+    return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even, NaN kept quiet
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+}  // namespace aqd

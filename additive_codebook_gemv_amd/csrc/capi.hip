@@ -1,0 +1,174 @@
+// C entry points of libaqd: argument validation, error reporting, dispatch.
+// Every check runs on the host before anything is enqueued, so a failing call
+// has no side effect on the device.
+#include <string>
+
+#include "aqd_internal.h"
+
+namespace aqd {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& s) { g_last_error = s; }
+
+static aqd_status fail(aqd_status st, const std::string& msg) {
+    g_last_error = msg;
+    return st;
+}
+
+static aqd_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return AQD_OK;
+    return fail(AQD_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+static bool aligned2(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
+
+constexpr int64_t MAX_DIM = int64_t(1) << 24;
+
+static aqd_status check_layer(const aqd_layer* L) {
+    if (!L) return fail(AQD_ERR_NULL, "layer is NULL");
+    if (L->group != GROUP || L->code_bits != 8)
+        return fail(AQD_ERR_UNSUPPORTED, "only group = 8 and code_bits = 8 are supported");
+    if (L->d_out < 0 || L->d_out > MAX_DIM) return fail(AQD_ERR_SHAPE, "d_out out of range");
+    if (L->d_in < 0 || L->d_in > MAX_DIM || L->d_in % GROUP != 0)
+        return fail(AQD_ERR_SHAPE, "d_in must be a multiple of 8 in [0, 2^24]");
+    if (L->M < 1 || L->M > MAX_M) return fail(AQD_ERR_SHAPE, "M must be in [1, 8]");
+    return AQD_OK;
+}
+
+}  // namespace aqd
+
+using namespace aqd;
+
+extern "C" {
+
+int aqd_abi_version(void) { return 1; }
+
+const char* aqd_status_string(int st) {
+    switch (st) {
+        case AQD_OK: return "ok";
+        case AQD_ERR_NULL: return "null pointer";
+        case AQD_ERR_SHAPE: return "bad shape";
+        case AQD_ERR_K: return "k outside [1, M]";
+        case AQD_ERR_BLOCK: return "bad Hadamard block";
+        case AQD_ERR_DTYPE: return "unsupported dtype";
+        case AQD_ERR_ALIGN: return "misaligned pointer";
+        case AQD_ERR_UNSUPPORTED: return "unsupported layer format";
+        case AQD_ERR_WORKSPACE: return "workspace missing or too small";
+        case AQD_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* aqd_last_error(void) { return g_last_error.c_str(); }
+
+size_t aqd_packed_codes_bytes(const aqd_layer* layer) {
+    if (check_layer(layer) != AQD_OK) return 0;
+    Geometry g = geometry(*layer);
+    return (size_t)(g.plane_bytes * g.M);
+}
+
+aqd_status aqd_pack_codes(const uint8_t* codes, uint8_t* packed, const aqd_layer* layer, void* stream) {
+    aqd_status st = check_layer(layer);
+    if (st != AQD_OK) return st;
+    Geometry g = geometry(*layer);
+    if (g.plane_bytes == 0) return AQD_OK;
+    if (!packed || (!codes && g.d_out * g.G > 0)) return fail(AQD_ERR_NULL, "codes or packed is NULL");
+    if (!aligned16(packed)) return fail(AQD_ERR_ALIGN, "packed must be 16-byte aligned");
+    return hip_status(launch_pack(codes, packed, g, (hipStream_t)stream), "aqd_pack_codes");
+}
+
+aqd_status aqd_unpack_codes(const uint8_t* packed, uint8_t* codes, const aqd_layer* layer, void* stream) {
+    aqd_status st = check_layer(layer);
+    if (st != AQD_OK) return st;
+    Geometry g = geometry(*layer);
+    if (g.d_out * g.G == 0) return AQD_OK;
+    if (!packed || !codes) return fail(AQD_ERR_NULL, "codes or packed is NULL");
+    if (!aligned16(packed)) return fail(AQD_ERR_ALIGN, "packed must be 16-byte aligned");
+    return hip_status(launch_unpack(packed, codes, g, (hipStream_t)stream), "aqd_unpack_codes");
+}
+
+aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype, int64_t batch,
+                               int64_t d_in, int32_t block, void* stream) {
+    if (in_dtype != AQD_F16 && in_dtype != AQD_BF16 && in_dtype != AQD_F32)
+        return fail(AQD_ERR_DTYPE, "in_dtype must be F16, BF16 or F32");
+    if (out_dtype != AQD_F16 && out_dtype != AQD_BF16 && out_dtype != AQD_F32 && out_dtype != AQD_BF16X2)
+        return fail(AQD_ERR_DTYPE, "out_dtype must be F16, BF16, F32 or BF16X2");
+    if (batch < 0 || batch > MAX_DIM || d_in < 0 || d_in > MAX_DIM)
+        return fail(AQD_ERR_SHAPE, "batch or d_in out of range");
+    if (block != 64 && block != 128 && block != 256)
+        return fail(AQD_ERR_BLOCK, "block must be 64, 128 or 256");
+    if (d_in % block != 0) return fail(AQD_ERR_BLOCK, "block must divide d_in");
+    if (batch * d_in == 0) return AQD_OK;
+    if (!x || !x_rot) return fail(AQD_ERR_NULL, "x or x_rot is NULL");
+    if (!aligned16(x) || !aligned16(x_rot)) return fail(AQD_ERR_ALIGN, "x and x_rot must be 16-byte aligned");
+    if (x == x_rot && (in_dtype != out_dtype || out_dtype == AQD_BF16X2))
+        return fail(AQD_ERR_DTYPE, "in-place rotation needs equal in/out dtypes");
+    return hip_status(launch_hadamard(x, x_rot, in_dtype, out_dtype, batch, d_in, block, (hipStream_t)stream),
+                      "aqd_hadamard_rotate");
+}
+
+size_t aqd_gemv_workspace_bytes(const aqd_layer* layer, int32_t batch) {
+    if (check_layer(layer) != AQD_OK || batch < 1 || batch > 8) return 0;
+    return gemv_workspace_bytes(geometry(*layer), batch);
+}
+
+static aqd_status check_product(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales,
+                                int32_t k, const void* x, const void* y, const aqd_layer* layer, void* ws,
+                                size_t ws_bytes, size_t ws_needed, bool* nothing_to_do) {
+    aqd_status st = check_layer(layer);
+    if (st != AQD_OK) return st;
+    if (k < 1 || k > layer->M) return fail(AQD_ERR_K, "k must be in [1, M]");
+    *nothing_to_do = layer->d_out == 0;
+    if (*nothing_to_do) return AQD_OK;
+    if (!y || !scales) return fail(AQD_ERR_NULL, "y or scales is NULL");
+    if (layer->d_in > 0 && (!packed || !codebooks || !x))
+        return fail(AQD_ERR_NULL, "packed_codes, codebooks or x_rot is NULL");
+    if ((packed && !aligned16(packed)) || (codebooks && !aligned16(codebooks)) || (x && !aligned16(x)))
+        return fail(AQD_ERR_ALIGN, "packed_codes, codebooks and x_rot must be 16-byte aligned");
+    if (!aligned2(scales) || !aligned2(y)) return fail(AQD_ERR_ALIGN, "scales and y must be 2-byte aligned");
+    if (ws_needed > 0) {
+        if (!ws || ws_bytes < ws_needed) return fail(AQD_ERR_WORKSPACE, "workspace missing or too small");
+        if (!aligned16(ws)) return fail(AQD_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    return AQD_OK;
+}
+
+aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales, int32_t k,
+                    const uint16_t* x_rot, uint16_t* y, int32_t batch, const aqd_layer* layer, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (batch < 1 || batch > 8) return fail(AQD_ERR_SHAPE, "aqd_gemv batch must be in [1, 8]");
+    bool nothing = false;
+    size_t need = layer ? aqd_gemv_workspace_bytes(layer, batch) : 0;
+    aqd_status st = check_product(packed_codes, codebooks, scales, k, x_rot, y, layer, workspace,
+                                  workspace_bytes, need, &nothing);
+    if (st != AQD_OK || nothing) return st;
+    return hip_status(launch_gemv(packed_codes, codebooks, scales, k, x_rot, y, batch, geometry(*layer),
+                                  workspace, (hipStream_t)stream),
+                      "aqd_gemv");
+}
+
+size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch) {
+    if (check_layer(layer) != AQD_OK || batch < 1 || batch > 64) return 0;
+    return gemm_sb_workspace_bytes(geometry(*layer), batch);
+}
+
+aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales,
+                                int32_t k, const void* x_rot, int x_dtype, float* y, int32_t batch,
+                                const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 1 || batch > 64) return fail(AQD_ERR_SHAPE, "aqd_gemm_small_batch batch must be in [1, 64]");
+    if (x_dtype != AQD_BF16 && x_dtype != AQD_BF16X2)
+        return fail(AQD_ERR_DTYPE, "x_dtype must be BF16 or BF16X2");
+    bool nothing = false;
+    size_t need = layer ? aqd_gemm_small_batch_workspace_bytes(layer, batch) : 0;
+    aqd_status st = check_product(packed_codes, codebooks, scales, k, x_rot, y, layer, workspace,
+                                  workspace_bytes, need, &nothing);
+    if (st != AQD_OK || nothing) return st;
+    if (!aligned16(y)) return fail(AQD_ERR_ALIGN, "y must be 16-byte aligned");
+    return hip_status(launch_gemm_sb(packed_codes, codebooks, scales, k, x_rot, x_dtype, y, batch,
+                                     geometry(*layer), workspace, (hipStream_t)stream),
+                      "aqd_gemm_small_batch");
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Online block Walsh-Hadamard rotation of the activation (Drop-by-Drop,
+// section 5: block-wise Walsh-Hadamard rotation; applied online at inference).
+//
+// One 64-wide wavefront transforms one block of b inputs.  Lane l holds the
+// elements l, l + 64, l + 128, ... of the block (b/64 per lane), so the six
+// butterfly stages whose partners are 1..32 apart cross lanes and the stages
+// 64 and 128 apart stay in registers.  Sums are fp32; the result is scaled by
+// 1/sqrt(b) and rounded once to the output type.  The butterfly network gives
+// the Sylvester-order matrix H[r][c] = (-1)^popcount(r & c).
+#include "aqd_internal.h"
+
+namespace aqd {
+
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t i) {
+    if (DT == AQD_F16) return h2f(static_cast<const uint16_t*>(p)[i]);
+    if (DT == AQD_BF16) return bf2f(static_cast<const uint16_t*>(p)[i]);
+    return static_cast<const float*>(p)[i];
+}
+
+template <int DT>
+__device__ __forceinline__ void store_from_f32(void* p, int64_t i, int64_t plane, float v) {
+    if (DT == AQD_F16) {
+        static_cast<uint16_t*>(p)[i] = f2h(v);
+    } else if (DT == AQD_BF16) {
+        static_cast<uint16_t*>(p)[i] = f2bf(v);
+    } else if (DT == AQD_F32) {
+        static_cast<float*>(p)[i] = v;
+    } else {  // AQD_BF16X2: hi plane then lo plane
+        const uint16_t hi = f2bf(v);
+        static_cast<uint16_t*>(p)[i] = hi;
+        static_cast<uint16_t*>(p)[plane + i] = f2bf(v - bf2f(hi));
+    }
+}
+
+template <int B>
+__device__ __forceinline__ float inv_sqrt_block() {
+    return B == 64 ? 0.125f : (B == 128 ? 0.0883883476483184405f : 0.0625f);
+}
+
+template <int B, int IN, int OUT>
+__global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y,
+                                                       int64_t d_in, int64_t n_blocks, int64_t plane) {
+    constexpr int E = B / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= n_blocks) return;
+    const int64_t per_row = d_in / B;
+    const int64_t base = (wave / per_row) * d_in + (wave % per_row) * B;
+    float v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = load_as_f32<IN>(x, base + e * 64 + lane);
+#pragma unroll
+    for (int h = 1; h < 64; h <<= 1) {
+        const bool upper = (lane & h) != 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float o = __shfl_xor(v[e], h);
+            v[e] = upper ? (o - v[e]) : (v[e] + o);
+        }
+    }
+#pragma unroll
+    for (int hb = 1; hb < E; hb <<= 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & hb) == 0) {
+                const float a = v[e], c = v[e | hb];
+                v[e] = a + c;
+                v[e | hb] = a - c;
+            }
+        }
+    }
+    const float sc = inv_sqrt_block<B>();
+#pragma unroll
+    for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e] * sc);
+}
+
+template <int B, int IN>
+static hipError_t launch_out(const void* x, void* y, int out_dt, int64_t batch, int64_t d_in, hipStream_t s) {
+    const int64_t n_blocks = batch * (d_in / B);
+    const int64_t plane = batch * d_in;
+    const dim3 grid((unsigned)((n_blocks + 3) / 4)), block(256);
+    switch (out_dt) {
+        case AQD_F16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F16>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
+        case AQD_BF16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
+        case AQD_F32: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F32>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
+        default: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16X2>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
+    }
+    return hipGetLastError();
+}
+
+template <int B>
+static hipError_t launch_in(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in, hipStream_t s) {
+    switch (in_dt) {
+        case AQD_F16: return launch_out<B, AQD_F16>(x, y, out_dt, batch, d_in, s);
+        case AQD_BF16: return launch_out<B, AQD_BF16>(x, y, out_dt, batch, d_in, s);
+        default: return launch_out<B, AQD_F32>(x, y, out_dt, batch, d_in, s);
+    }
+}
+
+hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in, int block,
+                           hipStream_t s) {
+    if (block == 64) return launch_in<64>(x, y, in_dt, out_dt, batch, d_in, s);
+    if (block == 128) return launch_in<128>(x, y, in_dt, out_dt, batch, d_in, s);
+    return launch_in<256>(x, y, in_dt, out_dt, batch, d_in, s);
+}
+
+}  // namespace aqd

@@ -1,0 +1,184 @@
+/*
+ * aqd.h -- C ABI of the additive-codebook decode kernels for AMD MI355X (gfx950).
+ *
+ * The operation is the decode-time linear layer of Drop-by-Drop
+ * ("Multi-Bitwidth Quantization for LLMs Using Additive Codebooks"):
+ *
+ *     y = s (.) ( What_k . xrot ),     xrot = (1/sqrt(b)) blockdiag(H_b, ..., H_b) x
+ *     What_k[i][8j + t] = sum_{m < k} C_m[ codes[i][j][m] ][t]
+ *
+ * - section 3.2: a row of weights is cut into groups of g = 8 consecutive
+ *   inputs; every group is the sum of one codeword per codebook, picked by
+ *   that group's code; rows are the concatenation of their group sums.
+ * - section 5: inference dequantizes from the first k <= M codebooks only
+ *   (the bitwidth knob), and a block-wise Walsh-Hadamard rotation is the
+ *   optional pre-processing whose counterpart is applied to the activation.
+ * - section 6 "Method Definitions": K codebooks of 8 bits per 8-wide group
+ *   give K bits per weight.
+ * - appendix "Estimating Model Size": fp16 codebooks [M][2^B][g], B-bit codes,
+ *   one fp16 scale per output row (shared by every k).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers are device pointers (hipMalloc / PyTorch CUDA tensors) owned by
+ *   the caller, except `layer`, which is a host pointer read during the call.
+ *   The library allocates no memory and keeps no per-call state; the only
+ *   global state is a per-device property cache filled on first use.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   Work is enqueued in order on that stream; calls return before it runs.
+ * - Arguments are validated on the host before anything is enqueued.  A call
+ *   that returns an error has enqueued nothing and written nothing.
+ *   aqd_last_error() gives a thread-local message for the last failure.
+ * - fp16 and bf16 values are passed as uint16_t bit patterns.  Every
+ *   conversion to fp16/bf16 rounds to nearest even.
+ * - No C++ exception crosses this interface.  The library is reentrant;
+ *   calls on different streams may run concurrently as long as they do not
+ *   write the same buffers.
+ */
+#ifndef AQD_H_
+#define AQD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum aqd_status {
+    AQD_OK = 0,
+    AQD_ERR_NULL = 1,        /* a required pointer is NULL */
+    AQD_ERR_SHAPE = 2,       /* d_out/d_in/batch/M out of range or not a supported multiple */
+    AQD_ERR_K = 3,           /* k outside [1, M] */
+    AQD_ERR_BLOCK = 4,       /* Hadamard block not in {64,128,256} or does not divide d_in */
+    AQD_ERR_DTYPE = 5,       /* unsupported dtype combination */
+    AQD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    AQD_ERR_UNSUPPORTED = 7, /* group != 8 or code_bits != 8 */
+    AQD_ERR_WORKSPACE = 8,   /* workspace missing or smaller than required */
+    AQD_ERR_HIP = 9          /* a HIP runtime call failed; see aqd_last_error() */
+} aqd_status;
+
+typedef enum aqd_dtype {
+    AQD_F16 = 0,     /* IEEE binary16 */
+    AQD_BF16 = 1,    /* bfloat16 */
+    AQD_F32 = 2,     /* IEEE binary32 */
+    AQD_BF16X2 = 3   /* a value v stored as two bf16 planes hi, lo (hi = bf16(v),
+                        lo = bf16(v - hi)); a [B][n] tensor is [2][B][n]: all hi, then all lo */
+} aqd_dtype;
+
+/* One quantized linear layer.  group and code_bits must both be 8
+ * (8-wide groups, 256 codewords per codebook). */
+typedef struct aqd_layer {
+    int64_t d_out;      /* output rows, >= 0 */
+    int64_t d_in;       /* inputs, a multiple of 8 */
+    int32_t M;          /* code planes (codebooks) stored, 1..8 */
+    int32_t group;      /* g, must be 8 */
+    int32_t code_bits;  /* B, must be 8 */
+} aqd_layer;
+
+/* Version of this interface (incremented on any incompatible change). */
+int aqd_abi_version(void);
+
+/* Static text for a status code. */
+const char* aqd_status_string(int status);
+
+/* Thread-local text describing the last failed call on this thread ("" if none). */
+const char* aqd_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Code layout (section 5: the first k codebooks are a complete model).
+ * Logical codes are [d_out][d_in/8][M] uint8, the index order of the AQLM
+ * reconstruction (row i, group j, codebook m).
+ *
+ * The packed layout is plane-major, so the codes a k-codebook product reads
+ * are exactly the first k planes.  A plane is a sequence of 1 KiB tiles, each
+ * covering 16 consecutive rows and 64 consecutive groups:
+ *
+ *   R = ceil(d_out / 16) row tiles, T = ceil((d_in/8) / 64) group tiles,
+ *   plane bytes P = R * T * 1024,
+ *   packed[m*P + (jt*R + it)*1024 + l*16 + r] = codes[16*it + r][64*jt + l][m]
+ *
+ * with zero bytes where 16*it + r >= d_out or 64*jt + l >= d_in/8 (padding
+ * that never contributes to a product).  Lane l of a 64-wide wavefront that
+ * loads 16 bytes of a tile receives the codes of one group for 16 rows.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the packed codes: M * P (see above); 0 for an invalid layer. */
+size_t aqd_packed_codes_bytes(const aqd_layer* layer);
+
+/* codes [d_out][d_in/8][M] -> packed tiles.  Byte exact; writes the padding zeros. */
+aqd_status aqd_pack_codes(const uint8_t* codes, uint8_t* packed, const aqd_layer* layer, void* stream);
+
+/* packed tiles -> codes [d_out][d_in/8][M].  Inverse of aqd_pack_codes. */
+aqd_status aqd_unpack_codes(const uint8_t* packed, uint8_t* codes, const aqd_layer* layer, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Online rotation of the activation (section 5, block-wise Walsh-Hadamard
+ * rotation; section 6, the rotation is applied online at inference).
+ *
+ * x_rot[n][beta*b + r] = (1/sqrt(b)) * sum_c H_b[r][c] * x[n][beta*b + c],
+ * H_b[r][c] = (-1)^popcount(r & c) (Sylvester order), blocks of b contiguous
+ * inputs starting at input 0, no sign flips.  Computed in fp32 by butterflies,
+ * then rounded once to out_dtype.
+ *
+ * x:      [batch][d_in] in in_dtype (AQD_F16, AQD_BF16 or AQD_F32).
+ * x_rot:  [batch][d_in] in out_dtype (AQD_F16, AQD_BF16, AQD_F32), or
+ *         [2][batch][d_in] for AQD_BF16X2.  May alias x only when in_dtype and
+ *         out_dtype are equal and not AQD_BF16X2.
+ * block:  b in {64, 128, 256}; b must divide d_in.  batch >= 0.
+ * Both pointers 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype,
+                               int64_t batch, int64_t d_in, int32_t block, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode GEMV, batch 1..8 (the lookup-and-accumulate hot path).
+ *
+ * y[n][i] = fp16( s_i * sum_j sum_{m<k} < C_m[codes[i][j][m]], x_rot[n][8j .. 8j+8) > )
+ *
+ * packed_codes: plane-major codes (see above); only the first k planes are read.
+ * codebooks:    fp16 [M][256][8]; only the first k codebooks are read.
+ * scales:       fp16 [d_out].
+ * x_rot:        fp16 [batch][d_in], the already rotated activation.
+ * y:            fp16 [batch][d_out].
+ * k:            1..M.  batch: 1..8.
+ * workspace:    device scratch of aqd_gemv_workspace_bytes(layer, batch) bytes
+ *               (may be NULL when that is 0).  It must be zero-filled before
+ *               its first use; every successful call leaves it zero-filled
+ *               again, so one buffer serves any number of calls on one stream
+ *               (calls that overlap in time need separate workspaces).
+ * Accumulation is fp32; the summation order is not specified.
+ * packed_codes, x_rot and workspace 16-byte aligned; codebooks 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t aqd_gemv_workspace_bytes(const aqd_layer* layer, int32_t batch);
+
+aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales,
+                    int32_t k, const uint16_t* x_rot, uint16_t* y, int32_t batch,
+                    const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Small-batch product, batch 1..64: code tiles are dequantized (codeword sums
+ * in fp32) into LDS as bf16 and multiplied on the bf16 matrix cores with fp32
+ * accumulation.  The weight tile is kept as bf16 hi + lo (two MFMA terms),
+ * and an AQD_BF16X2 activation adds its lo plane as a third term, so the
+ * product keeps close to fp32 accuracy.
+ *
+ * y[n][i] = s_i * sum_j sum_{m<k} < C_m[codes[i][j][m]], x_rot[n][8j .. 8j+8) >   (fp32)
+ *
+ * x_rot:  AQD_BF16 [batch][d_in] or AQD_BF16X2 [2][batch][d_in] (x_dtype).
+ * y:      fp32 [batch][d_out], overwritten.
+ * Other arguments as for aqd_gemv; workspace follows the same zero-filled
+ * contract with aqd_gemm_small_batch_workspace_bytes(layer, batch) bytes.
+ * ------------------------------------------------------------------------- */
+size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch);
+
+aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* codebooks,
+                                const uint16_t* scales, int32_t k, const void* x_rot, int x_dtype,
+                                float* y, int32_t batch, const aqd_layer* layer,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AQD_H_ */

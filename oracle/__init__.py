@@ -65,6 +65,8 @@ class Oracle:
         lib.oracle_reconstruct.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp]
         lib.oracle_linear.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp, _i64, _c_dp]
         lib.oracle_forward.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp, _i64, _i32, _c_dp]
+        lib.oracle_packed_bytes.restype = _i64
+        lib.oracle_packed_bytes.argtypes = [_i64, _i64, _i32]
         lib.oracle_pack_codes.argtypes = [_c_u8p, _i64, _i64, _i32, _c_u8p]
         lib.oracle_unpack_codes.argtypes = [_c_u8p, _i64, _i64, _i32, _c_u8p]
         lib.oracle_storage_bits.restype = ctypes.c_double
@@ -167,16 +169,19 @@ class Oracle:
         return y
 
     # -- layout ----------------------------------------------------------
+    def packed_bytes(self, d_out: int, G: int, M: int) -> int:
+        return int(self.lib.oracle_packed_bytes(d_out, G, M))
+
     def pack(self, codes: np.ndarray) -> np.ndarray:
         codes = np.ascontiguousarray(codes, dtype=np.uint8)
         d_out, G, M = codes.shape
-        out = np.empty(M * d_out * G, dtype=np.uint8)
+        out = np.empty(self.packed_bytes(d_out, G, M), dtype=np.uint8)
         assert self.lib.oracle_pack_codes(_ptr(codes, _c_u8p), d_out, G, M, _ptr(out, _c_u8p)) == 0
         return out
 
     def unpack(self, packed: np.ndarray, d_out: int, G: int, M: int) -> np.ndarray:
         packed = np.ascontiguousarray(packed, dtype=np.uint8)
-        assert packed.size == M * d_out * G
+        assert packed.size == self.packed_bytes(d_out, G, M)
         out = np.empty((d_out, G, M), dtype=np.uint8)
         assert self.lib.oracle_unpack_codes(_ptr(packed, _c_u8p), d_out, G, M, _ptr(out, _c_u8p)) == 0
         return out

@@ -331,19 +331,45 @@ int oracle_forward(const uint8_t *codes, const double *codebooks, const double *
 }
 
 /* ---------------------------------------------------------------------------
- * Packed code layout: plane-major, packed[m][i][j] = codes[i][j][m], so the
- * codes of the first k codebooks are the first k * d_out * (d_in/8) bytes
- * (section 5: the first k codebooks are a self-contained lower bitwidth).
+ * Packed code layout.  Plane-major, so the codes of the first k codebooks are
+ * a prefix of the buffer (section 5: the first k codebooks are a
+ * self-contained lower bitwidth).  Inside a plane the codes sit in 1 KiB
+ * tiles of 16 rows x 64 groups, tiles ordered by group tile then row tile,
+ * bytes inside a tile ordered by group then row; rows and groups beyond the
+ * layer are zero padding.  This tile order is the library's storage format
+ * (the pages fix only the prefix property), written out from its definition:
+ *   packed[m*P + (jt*R + it)*1024 + l*16 + r] = codes[16*it + r][64*jt + l][m]
  * ------------------------------------------------------------------------- */
+
+#define ORACLE_TILE_ROWS 16
+#define ORACLE_TILE_GROUPS 64
+
+static int64_t tiles_r(int64_t d_out) { return (d_out + ORACLE_TILE_ROWS - 1) / ORACLE_TILE_ROWS; }
+static int64_t tiles_g(int64_t G) { return (G + ORACLE_TILE_GROUPS - 1) / ORACLE_TILE_GROUPS; }
+
+int64_t oracle_packed_bytes(int64_t d_out, int64_t G, int32_t M)
+{
+    return (int64_t)M * tiles_r(d_out) * tiles_g(G) * ORACLE_TILE_ROWS * ORACLE_TILE_GROUPS;
+}
+
+static int64_t packed_offset(int64_t i, int64_t j, int32_t m, int64_t R, int64_t P)
+{
+    const int64_t it = i / ORACLE_TILE_ROWS, r = i % ORACLE_TILE_ROWS;
+    const int64_t jt = j / ORACLE_TILE_GROUPS, l = j % ORACLE_TILE_GROUPS;
+    return (int64_t)m * P + (jt * R + it) * (ORACLE_TILE_ROWS * ORACLE_TILE_GROUPS) + l * ORACLE_TILE_ROWS + r;
+}
 
 int oracle_pack_codes(const uint8_t *codes, int64_t d_out, int64_t G, int32_t M, uint8_t *packed)
 {
     if (d_out < 0 || G < 0 || M < 1)
         return -1;
+    const int64_t R = tiles_r(d_out);
+    const int64_t P = R * tiles_g(G) * ORACLE_TILE_ROWS * ORACLE_TILE_GROUPS;
+    memset(packed, 0, (size_t)(P * M));
     for (int32_t m = 0; m < M; ++m)
         for (int64_t i = 0; i < d_out; ++i)
             for (int64_t j = 0; j < G; ++j)
-                packed[((int64_t)m * d_out + i) * G + j] = codes[(i * G + j) * M + m];
+                packed[packed_offset(i, j, m, R, P)] = codes[(i * G + j) * M + m];
     return 0;
 }
 
@@ -351,10 +377,12 @@ int oracle_unpack_codes(const uint8_t *packed, int64_t d_out, int64_t G, int32_t
 {
     if (d_out < 0 || G < 0 || M < 1)
         return -1;
+    const int64_t R = tiles_r(d_out);
+    const int64_t P = R * tiles_g(G) * ORACLE_TILE_ROWS * ORACLE_TILE_GROUPS;
     for (int64_t i = 0; i < d_out; ++i)
         for (int64_t j = 0; j < G; ++j)
             for (int32_t m = 0; m < M; ++m)
-                codes[(i * G + j) * M + m] = packed[((int64_t)m * d_out + i) * G + j];
+                codes[(i * G + j) * M + m] = packed[packed_offset(i, j, m, R, P)];
     return 0;
 }
 

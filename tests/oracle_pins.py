@@ -306,17 +306,31 @@ def _byte_compare(a: np.ndarray, b: np.ndarray, what: str):
     assert bad.size == 0, f"{what}: {bad.size} bytes differ, first at {bad[:8].tolist()}"
 
 
+def _np_tiles(codes: np.ndarray) -> np.ndarray:
+    """Independent construction of the packed tiles with numpy reshapes:
+    pad to whole 16-row x 64-group tiles, then order [m][group tile][row tile][group][row]."""
+    d_out, G, M = codes.shape
+    R, T = -(-d_out // 16), -(-G // 64)
+    pad = np.zeros((R * 16, T * 64, M), dtype=np.uint8)
+    pad[:d_out, :G, :] = codes
+    t = pad.reshape(R, 16, T, 64, M)          # [it][r][jt][l][m]
+    return np.ascontiguousarray(t.transpose(4, 2, 0, 3, 1)).reshape(-1)
+
+
 def pin_pack_roundtrip_and_prefix(orc):
     g = _rng(60)
-    for d_out, G, M in ((3, 5, 4), (16, 32, 2), (7, 64, 3)):
+    for d_out, G, M in ((3, 5, 4), (16, 64, 2), (37, 130, 3), (1, 1, 1)):
         codes = g.integers(0, 256, size=(d_out, G, M), dtype=np.uint8)
         packed = orc.pack(codes)
+        _byte_compare(packed, _np_tiles(codes), "pack vs numpy tiles")
         _byte_compare(orc.unpack(packed, d_out, G, M), codes, "unpack(pack)")
+        plane = packed.size // M
         for k in range(1, M + 1):
-            _byte_compare(packed[: k * d_out * G], orc.pack(codes[:, :, :k]), f"prefix k={k}")
-        # plane m, row i, group j sits at byte (m*d_out + i)*G + j
-        m, i, j = M - 1, d_out - 1, G // 2
-        assert packed[(m * d_out + i) * G + j] == codes[i, j, m]
+            _byte_compare(packed[: k * plane], orc.pack(codes[:, :, :k]), f"prefix k={k}")
+        # a hand-located byte: plane m, row i, group j
+        m, i, j = M - 1, d_out - 1, G - 1
+        R = -(-d_out // 16)
+        assert packed[m * plane + ((j // 64) * R + i // 16) * 1024 + (j % 64) * 16 + i % 16] == codes[i, j, m]
 
 
 def pin_storage_worked_example(orc):

@@ -1,0 +1,160 @@
+"""The C ABI library on the host (no GPU needed).
+
+- libaqd.so loads and exports every function include/aqd.h declares;
+- argument validation rejects bad calls with the documented status before
+  anything is enqueued (every call here fails validation, so no kernel is
+  ever launched on a machine without a GPU);
+- the product library does not link or load the oracle.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import additive_codebook_gemv_amd as aqd
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aqd.h")
+
+OK, E_NULL, E_SHAPE, E_K, E_BLOCK, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(10)
+F16, BF16, F32, BF16X2 = 0, 1, 2, 3
+FAKE = 0x10000      # 16-byte aligned, never dereferenced: each call below fails validation first
+FAKE_ODD = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aqd_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return aqd.lib()
+
+
+def lay(d_out=64, d_in=256, M=2, group=8, bits=8):
+    return ctypes.byref(aqd.aqd_layer(d_out, d_in, M, group, bits))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 11, names
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(aqd._SIGNATURES), "binding and header disagree"
+
+
+def test_dynamic_symbol_table_matches_header():
+    out = subprocess.run(["nm", "-D", "--defined-only", aqd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (aqd_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings_and_version(L):
+    assert L.aqd_abi_version() == 1
+    for st in range(10):
+        assert L.aqd_status_string(st)
+    assert L.aqd_status_string(99) == b"unknown status"
+
+
+def test_packed_bytes_matches_oracle_layout(L):
+    orc = oracle.load()
+    for d_out, d_in, M in ((256, 256, 2), (4096, 14336, 4), (1000, 1000, 3), (1, 8, 1), (0, 128, 2)):
+        got = L.aqd_packed_codes_bytes(lay(d_out, d_in, M))
+        assert got == orc.packed_bytes(d_out, d_in // 8, M), (d_out, d_in, M)
+    assert L.aqd_packed_codes_bytes(lay(64, 100, 2)) == 0      # d_in not a multiple of 8
+    assert L.aqd_packed_codes_bytes(lay(64, 256, 2, group=4)) == 0
+
+
+def _gemv(L, k=1, batch=1, layer=None, packed=FAKE, cb=FAKE, s=FAKE, x=FAKE, y=FAKE, ws=None, ws_bytes=0):
+    return L.aqd_gemv(packed, cb, s, k, x, y, batch, layer if layer is not None else lay(), ws, ws_bytes, None)
+
+
+def test_gemv_rejects_bad_arguments(L):
+    assert _gemv(L, k=0) == E_K
+    assert _gemv(L, k=3) == E_K                       # M = 2
+    assert _gemv(L, batch=0) == E_SHAPE
+    assert _gemv(L, batch=9) == E_SHAPE
+    assert _gemv(L, layer=lay(d_in=100)) == E_SHAPE
+    assert _gemv(L, layer=lay(M=0)) == E_SHAPE
+    assert _gemv(L, layer=lay(M=9)) == E_SHAPE
+    assert _gemv(L, layer=lay(d_out=-1)) == E_SHAPE
+    assert _gemv(L, layer=lay(group=4)) == E_UNSUP
+    assert _gemv(L, layer=lay(bits=4)) == E_UNSUP
+    assert L.aqd_gemv(FAKE, FAKE, FAKE, 1, FAKE, FAKE, 1, None, None, 0, None) == E_NULL
+    assert _gemv(L, packed=None) == E_NULL
+    assert _gemv(L, cb=None) == E_NULL
+    assert _gemv(L, x=None) == E_NULL
+    assert _gemv(L, y=None) == E_NULL
+    assert _gemv(L, s=None) == E_NULL
+    assert _gemv(L, packed=FAKE_ODD) == E_ALIGN
+    assert _gemv(L, x=FAKE_ODD) == E_ALIGN
+    assert _gemv(L, cb=FAKE_ODD) == E_ALIGN
+    assert _gemv(L, y=FAKE + 1) == E_ALIGN
+    assert b"k must be" in (L.aqd_last_error() if _gemv(L, k=0) else b"")
+
+
+def test_empty_layer_is_a_no_op(L):
+    # d_out = 0: nothing to compute, every pointer may be NULL
+    assert L.aqd_gemv(None, None, None, 1, None, None, 1, lay(d_out=0), None, 0, None) == OK
+    assert L.aqd_gemm_small_batch(None, None, None, 1, None, BF16, None, 16, lay(d_out=0), None, 0, None) == OK
+    assert L.aqd_hadamard_rotate(None, None, F16, F16, 0, 256, 64, None) == OK
+    assert L.aqd_pack_codes(None, None, lay(d_out=0, d_in=0), None) == OK
+
+
+def test_small_batch_rejects_bad_arguments(L):
+    def sb(k=1, batch=16, x_dt=BF16X2, layer=None, y=FAKE, x=FAKE):
+        return L.aqd_gemm_small_batch(FAKE, FAKE, FAKE, k, x, x_dt, y, batch, layer if layer is not None else lay(),
+                                      None, 0, None)
+    assert sb(batch=0) == E_SHAPE
+    assert sb(batch=65) == E_SHAPE
+    assert sb(k=0) == E_K
+    assert sb(x_dt=F16) == E_DTYPE
+    assert sb(x_dt=F32) == E_DTYPE
+    assert sb(y=FAKE + 4) == E_ALIGN
+    assert sb(x=None) == E_NULL
+
+
+def test_hadamard_rejects_bad_arguments(L):
+    def rot(x=FAKE, y=FAKE + 4096, i=F16, o=F16, batch=1, d_in=256, b=64):
+        return L.aqd_hadamard_rotate(x, y, i, o, batch, d_in, b, None)
+    assert rot(b=32) == E_BLOCK
+    assert rot(b=512) == E_BLOCK
+    assert rot(b=128, d_in=192) == E_BLOCK
+    assert rot(i=BF16X2) == E_DTYPE
+    assert rot(i=7) == E_DTYPE
+    assert rot(o=9) == E_DTYPE
+    assert rot(batch=-1) == E_SHAPE
+    assert rot(x=None) == E_NULL
+    assert rot(y=FAKE_ODD) == E_ALIGN
+    assert rot(y=FAKE, i=F16, o=F32) == E_DTYPE          # in place with different dtypes
+    assert rot(y=FAKE, i=F16, o=BF16X2) == E_DTYPE
+
+
+def test_pack_rejects_bad_arguments(L):
+    assert L.aqd_pack_codes(FAKE, None, lay(), None) == E_NULL
+    assert L.aqd_pack_codes(FAKE, FAKE_ODD, lay(), None) == E_ALIGN
+    assert L.aqd_unpack_codes(FAKE_ODD, FAKE, lay(), None) == E_ALIGN
+    assert L.aqd_pack_codes(FAKE, FAKE, lay(group=16), None) == E_UNSUP
+
+
+def test_product_does_not_link_or_load_the_oracle():
+    deps = subprocess.run(["readelf", "-d", aqd.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "oracle" not in deps
+    pkg = os.path.join(ROOT, "additive_codebook_gemv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in src and "from oracle" not in src and "liboracle" not in src, f
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(aqd, "_lib", None)
+    monkeypatch.setattr(aqd, "LIB_PATH", str(tmp_path / "libaqd.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        aqd.lib()

@@ -1,0 +1,286 @@
+"""Parity of the HIP path with the fp64 CPU oracle (needs an MI355X).
+
+Every comparison calls the product through the C ABI (the Python binding is
+argument marshalling only) and the oracle on the same seeded inputs:
+- integer / byte work (code packing) must be bit-exact;
+- floating point must be within 2e-3 max normwise relative error
+  (max |gpu - oracle| / max |oracle|) of the fp64 oracle, for the GEMV both
+  against the oracle fed the GPU's own fp16 rotated activation and against the
+  pure fp64 path from the raw activation;
+- inputs built so that every partial sum is exact (dyadic codewords, +-1
+  activations) must give bit-identical results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import additive_codebook_gemv_amd as aqd
+import oracle
+import workloads as wl
+from tests.gpu_util import TOL, dev, normwise, record, rms_rel, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    o = oracle.load()
+    o.set_threads(16)
+    return o
+
+
+def _layer_dev(codes, cb, s):
+    return to_dev(codes), to_dev(cb), to_dev(s)
+
+
+def _f16_ulp(v: np.ndarray) -> np.ndarray:
+    a = np.abs(v).astype(np.float64)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+# ---------------------------------------------------------------------------
+# packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,M", [(256, 256, 2), (4096, 14336, 4), (1000, 1000, 3), (1, 8, 1), (17, 520, 8)])
+def test_pack_bit_exact(orc, d_out, d_in, M):
+    g = wl.rng(7, kind="codes", extra=d_out + d_in + M)
+    codes = wl.gen_codes(g, d_out, d_in, M)
+    packed = aqd.aqd_pack_codes(to_dev(codes))
+    ref = orc.pack(codes)
+    got = packed.cpu().numpy()
+    assert got.size == ref.size
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8].tolist()}"
+    back = aqd.aqd_unpack_codes(packed, d_out, d_in, M).cpu().numpy()
+    assert np.array_equal(back, codes)
+    # the first k planes are exactly the packing of the first k codebooks
+    plane = got.size // M
+    for k in range(1, M + 1):
+        pk = aqd.aqd_pack_codes(to_dev(np.ascontiguousarray(codes[:, :, :k]))).cpu().numpy()
+        assert np.array_equal(pk, got[: k * plane]), k
+
+
+# ---------------------------------------------------------------------------
+# rotation
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_rotation_matches_oracle(orc, block):
+    d_in = 14336 if block == 256 else 4096
+    x = wl.gen_x(wl.rng(11, extra=block), 8, d_in, "f16")
+    xd = to_dev(x)
+    ref = orc.rotate(x, block)
+    f32 = aqd.aqd_hadamard_rotate(xd, block, aqd.AQD_F32).cpu().numpy()
+    err32 = normwise(f32, ref)
+    assert err32 < 1e-6, err32
+    f16 = aqd.aqd_hadamard_rotate(xd, block, aqd.AQD_F16).cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(f16 - ref) <= _f16_ulp(ref)), "fp16 output more than one ulp from the exact rotation"
+    x2 = aqd.aqd_hadamard_rotate(xd, block, aqd.AQD_BF16X2).float().cpu().numpy().astype(np.float64)
+    err2 = normwise(x2[0] + x2[1], ref)
+    assert err2 < 2.0 ** -15, err2
+    record(test="rotation", block=block, err_f32=err32, err_bf16x2=err2)
+
+
+@pytest.mark.parametrize("block", [64, 256])
+def test_rotation_bit_exact_on_integers(orc, block):
+    """Integer inputs with b = 64 or 256 (1/sqrt(b) a power of two): every sum is exact."""
+    g = wl.rng(12, extra=block)
+    x = g.integers(-8, 9, size=(3, 4 * block)).astype(np.float16)
+    got = aqd.aqd_hadamard_rotate(to_dev(x), block, aqd.AQD_F16).cpu().numpy().view(np.uint16)
+    ref = orc.encode(orc.rotate(x, block), "f16")
+    assert np.array_equal(got, ref)
+
+
+def test_rotation_bf16_input_and_in_place(orc):
+    x = wl.gen_x(wl.rng(13), 4, 1024, "bf16")
+    ref = orc.rotate(x, 128, "bf16")
+    got = aqd.aqd_hadamard_rotate(to_dev(x, bf16_bits=True), 128, aqd.AQD_F32).cpu().numpy()
+    assert normwise(got, ref) < 1e-6
+    xf = wl.gen_x(wl.rng(14), 2, 512, "f16")
+    t = to_dev(xf)
+    out = aqd.aqd_hadamard_rotate(t, 64, aqd.AQD_F16, out=t)        # in place
+    assert out.data_ptr() == t.data_ptr()
+    assert np.all(np.abs(t.cpu().numpy().astype(np.float64) - orc.rotate(xf, 64)) <= _f16_ulp(orc.rotate(xf, 64)))
+
+
+# ---------------------------------------------------------------------------
+# GEMV (batch 1..8)
+# ---------------------------------------------------------------------------
+
+def _check_gemv_layer(orc, cid, lin, rows=None):
+    bmax = max(lin.batches)
+    codes, cb, s, x = wl.layer_inputs(cid, lin, batch=bmax)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xr = aqd.aqd_hadamard_rotate(to_dev(x), lin.block, aqd.AQD_F16)
+    xr_np = xr.cpu().numpy()
+    sel = slice(None) if rows is None else rows
+    c_o, s_o = (codes, s) if rows is None else (codes[rows], s[rows])
+    for k in lin.ks:
+        ref_lin = orc.linear(c_o, cb, s_o, k, xr_np)
+        ref_full = orc.forward(c_o, cb, s_o, k, x, lin.block)
+        for B in lin.batches:
+            y = aqd.aqd_gemv(packed, cbdev, sdev, k, xr[:B].contiguous(), lin.d_out, lin.d_in, lin.M)
+            y = y.cpu().numpy().astype(np.float64)[:, sel]
+            e_lin = normwise(y, ref_lin[:B])
+            e_full = normwise(y, ref_full[:B])
+            record(test="gemv", cfg=cid, layer=lin.name, k=k, batch=B, err=e_full, err_same_input=e_lin,
+                   rms=rms_rel(y, ref_full[:B]), sampled_rows=None if rows is None else len(rows))
+            assert e_lin <= TOL and e_full <= TOL, (lin.name, k, B, e_lin, e_full)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_gemv_config(orc, cid):
+    for lin in wl.config(cid):
+        _check_gemv_layer(orc, cid, lin)
+
+
+@pytest.mark.parametrize("name", ["gate14336x4096", "up14336x4096", "down4096x14336"])
+def test_gemv_mlp_config(orc, name):
+    lin = [l for l in wl.config(3) if l.name == name][0]
+    _check_gemv_layer(orc, 3, lin)
+
+
+def test_gemv_stack_sampled(orc):
+    """32-layer stack: three layers, all seven projections, at their seeded k; 96 sampled rows each."""
+    lins = wl.config(4)
+    g = np.random.Generator(np.random.PCG64(404))
+    for lin in [l for l in lins if l.layer in (0, 17, 31)]:
+        rows = np.sort(g.choice(lin.d_out, size=96, replace=False))
+        _check_gemv_layer(orc, 4, lin, rows=rows)
+
+
+@pytest.mark.parametrize("d_out,d_in,M,batches", [
+    (1000, 1000, 3, (1, 3, 8)),       # ragged rows (not a multiple of 16) and groups (not a multiple of 64)
+    (1, 8, 1, (1, 2)),                # one row, one group
+    (33, 4096, 8, (1, 5)),            # M = 8 codebooks, every k
+    (2048, 512, 2, (7,)),
+])
+def test_gemv_edge_shapes(orc, d_out, d_in, M, batches):
+    g = wl.rng(21, extra=d_out * 7 + d_in + M)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    xr = wl.gen_x(g, max(batches), d_in, "f16")          # stands for an already rotated activation
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    for k in range(1, M + 1):
+        ref = orc.linear(codes, cb, s, k, xr)
+        for B in batches:
+            y = aqd.aqd_gemv(packed, cbdev, sdev, k, to_dev(xr[:B]), d_out, d_in, M).cpu().numpy()
+            e = normwise(y, ref[:B])
+            record(test="gemv_edge", shape=[d_out, d_in, M], k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
+
+
+def test_gemv_empty_input_gives_zero():
+    d_out = 40
+    s = to_dev(np.ones(d_out, dtype=np.float16))
+    y = torch.full((2, d_out), 7.0, dtype=torch.float16, device=dev())
+    aqd.aqd_gemv(torch.empty(0, dtype=torch.uint8, device=dev()), torch.empty(0, dtype=torch.float16, device=dev()),
+                 s, 1, torch.empty((2, 0), dtype=torch.float16, device=dev()), d_out, 0, 2, out=y)
+    assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("d_out,d_in,M", [(256, 256, 2), (100, 1000, 4)])
+def test_gemv_dyadic_bit_exact(orc, d_out, d_in, M):
+    codes, cb, s, x = wl.dyadic_case(wl.rng(31, extra=d_out), d_out, d_in, M, batch=8)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    for k in range(1, M + 1):
+        ref = orc.linear(codes, cb, s, k, x)
+        assert np.max(np.abs(ref)) < 512          # every value and partial sum is exact in fp16/fp32
+        for B in (1, 8):
+            y = aqd.aqd_gemv(packed, cbdev, sdev, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()
+            assert np.array_equal(y.astype(np.float64), ref[:B]), (k, B)
+
+
+def test_gemv_prefix_property(orc):
+    """Keeping k codebooks equals keeping all four with codebooks k.. zeroed."""
+    lin = wl.config(2)[0]
+    codes, cb, s, x = wl.layer_inputs(2, lin)
+    cdev, sdev = to_dev(codes), to_dev(s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xr = to_dev(wl.gen_x(wl.rng(41), 1, lin.d_in, "f16"))
+    for k in (1, 2, 3):
+        cbz = cb.copy()
+        cbz[k:] = 0
+        yk = aqd.aqd_gemv(packed, to_dev(cb), sdev, k, xr, lin.d_out, lin.d_in, 4).cpu().numpy().astype(np.float64)
+        yz = aqd.aqd_gemv(packed, to_dev(cbz), sdev, 4, xr, lin.d_out, lin.d_in, 4).cpu().numpy().astype(np.float64)
+        assert normwise(yz, yk) <= 1e-3, k
+
+
+def test_gemv_rejects_bad_k_on_device():
+    lin = wl.config(1)[0]
+    codes, cb, s, x = wl.layer_inputs(1, lin)
+    with pytest.raises(aqd.AqdError) as ei:
+        aqd.aqd_gemv(aqd.aqd_pack_codes(to_dev(codes)), to_dev(cb), to_dev(s), 3, to_dev(x), 256, 256, 2)
+    assert ei.value.status == 3
+
+
+# ---------------------------------------------------------------------------
+# small batch on the matrix cores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["gate14336x4096_sb", "down4096x14336_sb"])
+def test_small_batch_config(orc, name):
+    lin = [l for l in wl.config(5) if l.name == name][0]
+    codes, cb, s, x = wl.layer_inputs(5, lin, batch=64)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xd = to_dev(x, bf16_bits=True)
+    xr = aqd.aqd_hadamard_rotate(xd, lin.block, aqd.AQD_BF16X2)
+    for k in lin.ks:
+        ref = orc.forward(codes, cb, s, k, x, lin.block, "bf16")
+        for B in lin.batches:
+            xb = xr[:, :B].contiguous()
+            y = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xb, lin.d_out, lin.d_in, 4, aqd.AQD_BF16X2)
+            e = normwise(y.cpu().numpy(), ref[:B])
+            record(test="small_batch", layer=name, k=k, batch=B, err=e, rms=rms_rel(y.cpu().numpy(), ref[:B]))
+            assert e <= TOL, (k, B, e)
+
+
+@pytest.mark.parametrize("d_out,d_in,M,batches", [(1000, 1000, 3, (1, 17, 64)), (16, 64, 1, (16,))])
+def test_small_batch_edge_shapes(orc, d_out, d_in, M, batches):
+    g = wl.rng(51, extra=d_out + d_in)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    x = g.standard_normal((max(batches), d_in)).astype(np.float32)
+    xt = torch.from_numpy(x).to(dev())
+    hi = xt.to(torch.bfloat16)
+    lo = (xt - hi.float()).to(torch.bfloat16)
+    xx = torch.stack([hi, lo])                       # AQD_BF16X2 operand of an already rotated activation
+    x_exact = hi.double().cpu().numpy() + lo.double().cpu().numpy()
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    for k in range(1, M + 1):
+        ref = orc.linear(codes, cb, s, k, x_exact)
+        for B in batches:
+            y = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xx[:, :B].contiguous(), d_out, d_in, M,
+                                         aqd.AQD_BF16X2).cpu().numpy()
+            e = normwise(y, ref[:B])
+            record(test="small_batch_edge", shape=[d_out, d_in, M], k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
+
+
+def test_small_batch_dyadic_bit_exact(orc):
+    d_out, d_in, M = 200, 512, 2
+    codes, cb, s, x = wl.dyadic_case(wl.rng(61), d_out, d_in, M, batch=32)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xb = torch.from_numpy(x.astype(np.float32)).to(dev()).to(torch.bfloat16).contiguous()
+    for k in (1, 2):
+        ref = orc.linear(codes, cb, s, k, x)
+        y = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xb, d_out, d_in, M, aqd.AQD_BF16).cpu().numpy()
+        assert np.array_equal(y.astype(np.float64), ref), k
+
+
+def test_quantized_linear_forward(orc):
+    """The resident-layer helper: rotate + product, both batch regimes."""
+    lin = wl.config(2)[0]
+    codes, cb, s, _ = wl.layer_inputs(2, lin)
+    q = aqd.QuantizedLinear(to_dev(codes), to_dev(cb), to_dev(s), lin.block)
+    for B in (1, 4, 16):
+        x = wl.gen_x(wl.rng(71, extra=B), B, lin.d_in, "f16")
+        y = q.forward(to_dev(x), 3).float().cpu().numpy()
+        ref = orc.forward(codes, cb, s, 3, x, lin.block)
+        assert normwise(y, ref) <= TOL, B

@@ -37,10 +37,12 @@ MUTANTS = {
     "encode_truncates": ("q = nearbyint(ldexp(a, mant - ex));", "q = floor(ldexp(a, mant - ex));"),
     "encode_overflow_bound": ("if (ex + bias >= emax_field)", "if (ex + bias > emax_field)"),
     "bf16_encode_width": ("encode_mag(fabs(v), 7, 127, 255)", "encode_mag(fabs(v), 8, 127, 255)"),
-    "pack_planes_interleaved": ("packed[((int64_t)m * d_out + i) * G + j] = codes[(i * G + j) * M + m];",
-                                "packed[((int64_t)i * M + m) * G + j] = codes[(i * G + j) * M + m];"),
-    "unpack_groups_reversed": ("codes[(i * G + j) * M + m] = packed[((int64_t)m * d_out + i) * G + j];",
-                               "codes[(i * G + j) * M + m] = packed[((int64_t)m * d_out + i) * G + (G - 1 - j)];"),
+    "pack_tile_transposed": ("+ l * ORACLE_TILE_ROWS + r;", "+ r * ORACLE_TILE_GROUPS + l;"),
+    "pack_tiles_row_major": ("(jt * R + it)", "(it * tiles_g(P) + jt)"),
+    "pack_planes_interleaved": ("packed[packed_offset(i, j, m, R, P)] = codes[(i * G + j) * M + m];",
+                                "packed[packed_offset(i, j, 0, R, P) * M + m] = codes[(i * G + j) * M + m];"),
+    "unpack_planes_reversed": ("codes[(i * G + j) * M + m] = packed[packed_offset(i, j, m, R, P)];",
+                               "codes[(i * G + j) * M + m] = packed[packed_offset(i, j, M - 1 - m, R, P)];"),
     "storage_scale_bits": ("(double)d_out * 16.0;", "(double)d_out * 8.0;"),
     "storage_codebook_bits": ("ldexp(1.0, B) * 16.0", "ldexp(1.0, B) * 8.0"),
 }
