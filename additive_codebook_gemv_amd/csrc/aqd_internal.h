@@ -54,6 +54,10 @@ hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_
 size_t gemv_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
+size_t gemv_lut_workspace_bytes(const Geometry& g);
+bool gemv_lut_supported(const Geometry& g, int batch);
+hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                           const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,

@@ -1,0 +1,345 @@
+// Batch-1 decode GEMV through per-group lookup tables.
+//
+// Drop-by-Drop ("Multi-Bitwidth Quantization for LLMs Using Additive
+// Codebooks"), section 3.2 and section 5: a weight group is the sum of the
+// codewords its k codes select, so its contribution to an output row is
+//     sum_{m<k} T_{m,j}[code(i,j,m)],   T_{m,j}[c] = < C_m[c], xrot[8j .. 8j+8) >.
+// For batch 1 every row reuses the same 256-entry table per (group, codebook),
+// so the product becomes one 2-byte table lookup and half an fp32 add per code
+// byte instead of a 16-byte codeword gather and four dot2 steps.
+//
+// Work split.  A "slot" is one (group tile, codebook) pair: 64 groups of one
+// plane.  A workgroup owns a slice of 4 consecutive slots and a block of row
+// tiles.  It builds the 4 x 64 tables of its slice with matrix-core products
+// (v_mfma_f32_32x32x8_f16: 32 codewords x 8 elements times 8 elements x 32
+// groups), stores them as fp16 in LDS, then streams its row tiles: lane l of a
+// wave loads the 16 codes of group l for 16 rows for each slot (one coalesced
+// 1 KiB tile per slot), looks up the four table entries of every row and adds
+// them in fp32.
+//
+// LDS layout.  Entry (slot s, codeword c, lane l) is the fp16 at byte
+//     (s/2)*64K + c*256 + l*4 + 2*(s%2),
+// so lane l only ever touches LDS bank l (mod the bank count): the random
+// codes never collide, and the address is built from the code byte with one
+// v_perm_b32 (code -> byte 1, lane offset -> byte 0, slot pair -> byte 2).
+//
+// Reduction.  Each lane holds 16 row partials (its group, all slots).  A
+// transposing butterfly (permlane32 swap, permlane16 swap, row mirror, half
+// row mirror, quad DPP) leaves row (l >> 2) summed over the wave in lane l.
+// Each slice adds its row sums to a per-row accumulator in the workspace as
+// 64-bit fixed point (device-scope integer atomics, so the total is exact and
+// independent of arrival order); the last workgroup of a row block to finish
+// (counted with an atomic counter) takes each total with one atomic exchange,
+// scales by s_i, rounds to fp16 and writes y.  The exchange and a counter reset
+// leave the workspace zero for the next call; results are reproducible bit for
+// bit.
+#include "aqd_internal.h"
+
+namespace aqd {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
+
+constexpr int LUT_SLOTS = 4;
+constexpr int LUT_PAIR_BYTES = CODEWORDS * 64 * 4;           // 64 KiB
+constexpr int LUT_BYTES = (LUT_SLOTS / 2) * LUT_PAIR_BYTES;  // 128 KiB
+constexpr int LUT_CUS = 256;                                  // one 128 KiB workgroup per CU
+constexpr int LUT_WAVES = 16;
+constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles a wave keeps in flight
+
+struct LutArgs {
+    const uint8_t* packed;
+    const uint16_t* codebooks;
+    const uint16_t* scales;
+    const uint16_t* x;
+    uint16_t* y;
+    unsigned long long* acc;  // workspace: int64 [d_out] fixed-point row sums, zero between calls
+    uint32_t* counters;  // workspace: uint32 [row blocks], zero between calls
+    int64_t d_out, G, n_rt, n_gt, plane_bytes;
+    int k, n_slots, slices, tiles_per_block;
+};
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load of codes that are read exactly once.
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t lut_addr(uint32_t code_dword, uint32_t base, int byte) {
+    // byte 0 <- base byte 0 (lane offset), byte 1 <- code byte `byte`, byte 2 <- base byte 2 (slot pair)
+    return __builtin_amdgcn_perm(code_dword, base, 0x0C020000u | ((uint32_t)(4 + byte) << 8));
+}
+
+// Row sums travel between workgroups as two's-complement fixed point with 32
+// fraction bits (|sum| < 2^31), so their total is exact and order independent.
+constexpr double FIX_ONE = 4294967296.0;  // 2^32
+constexpr double FIX_MAX = 2147483647.0 * 4294967296.0;
+
+__device__ __forceinline__ unsigned long long to_fixed(float v) {
+    double d = (double)v * FIX_ONE;
+    d = d > FIX_MAX ? FIX_MAX : (d < -FIX_MAX ? -FIX_MAX : d);
+    return (unsigned long long)__double2ll_rn(d);
+}
+
+__device__ __forceinline__ float from_fixed(unsigned long long u) {
+    return (float)((double)(long long)u * (1.0 / FIX_ONE));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float2 swap32(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float2 swap16(float a, float b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// v[r] = partial of row r in this lane.  Returns, in lane l, the sum over the
+// 64 lanes of row (l >> 2).
+__device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {          // lanes 0-31 keep row i, lanes 32-63 keep row i+8
+        const float2 s = swap32(v[i], v[i + 8]);
+        a[i] = s.x + s.y;
+    }
+    float b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {          // even 16-lane rows keep i, odd rows keep i+4
+        const float2 s = swap16(a[i], a[i + 4]);
+        b[i] = s.x + s.y;
+    }
+    const bool lo8 = (lane & 8) == 0;      // partner lane j <-> 15-j inside 16 lanes
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = lo8 ? b[i] : b[i + 2];
+        const float send = lo8 ? b[i + 2] : b[i];
+        c[i] = keep + dpp<0x140>(send);
+    }
+    const bool lo4 = (lane & 4) == 0;      // partner lane j <-> 7-j inside 8 lanes
+    const float keep = lo4 ? c[0] : c[1];
+    const float send = lo4 ? c[1] : c[0];
+    float d = keep + dpp<0x141>(send);
+    d += dpp<0xB1>(d);                     // quad: lanes 4q..4q+3 hold the same row
+    d += dpp<0x4E>(d);
+    return d;
+}
+
+template <int WAVES, int K>
+__global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
+    __shared__ __align__(16) uint8_t lds[LUT_BYTES + 16];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int slice = blockIdx.x % p.slices;
+    const int rb = blockIdx.x / p.slices;
+    const int64_t t0 = (int64_t)rb * p.tiles_per_block;
+    const int64_t t1 = t0 + p.tiles_per_block < p.n_rt ? t0 + p.tiles_per_block : p.n_rt;
+
+    // slot s of this slice: q = slice*4 + s -> group tile q / K, codebook q % K.
+    // Every load below is unconditional (inactive slots, padding groups and
+    // missing tiles read a valid address and the value is replaced by zero), so
+    // the compiler can wait for exactly the loads a step needs.
+    int64_t slot_off[LUT_SLOTS];
+    bool slot_on[LUT_SLOTS];
+#pragma unroll
+    for (int s = 0; s < LUT_SLOTS; ++s) {
+        const int q = slice * LUT_SLOTS + s;
+        slot_on[s] = q < p.n_slots;
+        const int qq = slot_on[s] ? q : 0;
+        slot_off[s] = (int64_t)(qq % K) * p.plane_bytes + (int64_t)(qq / K) * p.n_rt * TILE_BYTES + lane * TILE_ROWS;
+    }
+
+    // ---- table operands first (loads complete in order)
+    constexpr int ITEMS = 32 / WAVES;
+    uint2 av[ITEMS][2], bv[ITEMS][2];
+    bool bok[ITEMS][2];
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) {
+        const int item = wave + u * WAVES;
+        const int cb = (item >> 1) & 7, gb = item & 1, pair = item >> 4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int q = slice * LUT_SLOTS + 2 * pair + h;
+            const int qq = q < p.n_slots ? q : 0;
+            const int e0 = 4 * (lane >> 5);
+            const int c = cb * 32 + (lane & 31);
+            const int64_t g = (int64_t)(qq / K) * TILE_GROUPS + gb * 32 + (lane & 31);
+            bok[u][h] = q < p.n_slots && g < p.G;
+            const int64_t gc = g < p.G ? g : p.G - 1;
+            av[u][h] = *reinterpret_cast<const uint2*>(p.codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
+            bv[u][h] = *reinterpret_cast<const uint2*>(p.x + gc * GROUP + e0);
+        }
+    }
+
+    // ---- then every code tile of this wave (at most LUT_TILES_PER_WAVE), so the
+    // wave's whole share of the code stream is in flight while the tables are built
+    uint4 codes[LUT_TILES_PER_WAVE][LUT_SLOTS];
+#pragma unroll
+    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+        const int64_t it = t0 + wave + (int64_t)u * WAVES;
+        const int64_t itc = it < t1 ? it : t0;
+#pragma unroll
+        for (int s = 0; s < LUT_SLOTS; ++s) codes[u][s] = load_stream(p.packed + slot_off[s] + itc * TILE_BYTES);
+    }
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            if (!bok[u][h]) bv[u][h] = make_uint2(0u, 0u);     // zero activation -> zero table entries
+        }
+
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u) {
+        const int item = wave + u * WAVES;
+        const int pair = item >> 4, cb = (item >> 1) & 7, gb = item & 1;
+        floatx16_t t[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[h][r] = 0.f;
+            t[h] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(half4_t, av[u][h]),
+                                                        __builtin_bit_cast(half4_t, bv[u][h]), t[h], 0, 0, 0);
+        }
+        const int gl = gb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = cb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const half2_t v = half2_t{(_Float16)t[0][r], (_Float16)t[1][r]};
+            *reinterpret_cast<half2_t*>(lds + pair * LUT_PAIR_BYTES + c * 256 + gl * 4) = v;
+        }
+    }
+    __syncthreads();
+
+    uint32_t base[LUT_SLOTS];
+#pragma unroll
+    for (int s = 0; s < LUT_SLOTS; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
+    const half2_t ones = half2_t{(_Float16)1.0f, (_Float16)1.0f};
+
+#pragma unroll
+    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+        const int64_t it = t0 + wave + (int64_t)u * WAVES;
+        if (it >= t1) break;                   // uniform across the wave
+        float rows[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int pr = 0; pr < LUT_SLOTS / 2; ++pr) {
+                const uint4& c0 = codes[u][2 * pr];
+                const uint4& c1 = codes[u][2 * pr + 1];
+                const uint32_t w0 = (r >> 2) == 0 ? c0.x : (r >> 2) == 1 ? c0.y : (r >> 2) == 2 ? c0.z : c0.w;
+                const uint32_t w1 = (r >> 2) == 0 ? c1.x : (r >> 2) == 1 ? c1.y : (r >> 2) == 2 ? c1.z : c1.w;
+                const uint32_t a0 = lut_addr(w0, base[2 * pr], r & 3);
+                const uint32_t a1 = lut_addr(w1, base[2 * pr + 1], r & 3);
+                const half2_t v = half2_t{*reinterpret_cast<const _Float16*>(lds + a0),
+                                          *reinterpret_cast<const _Float16*>(lds + a1)};
+                a = __builtin_amdgcn_fdot2(v, ones, a, false);
+            }
+            rows[r] = a;
+        }
+        const float sum = fold_rows(rows, lane);
+        const int64_t row = it * TILE_ROWS + (lane >> 2);
+        if ((lane & 3) == 0 && row < p.d_out) atomicAdd(p.acc + row, to_fixed(sum));
+    }
+
+    // ---- the last slice to finish a row block writes it out.  Every slice's
+    // row sums were added as fixed-point integers, so the total does not depend
+    // on the order the slices arrive in.  Each wave waits until its atomics are
+    // performed before the counter is bumped; the last workgroup takes each row
+    // total with one exchange, which also clears the accumulator for the next call.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t* flag = reinterpret_cast<uint32_t*>(lds + LUT_BYTES);
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(p.counters + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = (done == (uint32_t)(p.slices - 1)) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (*flag) {
+        const int64_t r0 = t0 * TILE_ROWS;
+        const int64_t r1 = t1 * TILE_ROWS < p.d_out ? t1 * TILE_ROWS : p.d_out;
+        for (int64_t i = r0 + tid; i < r1; i += 64 * WAVES) {
+            const unsigned long long t = atomicExch(p.acc + i, 0ull);
+            p.y[i] = f2h(h2f(p.scales[i]) * from_fixed(t));
+        }
+        if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---- host side ---------------------------------------------------------------
+
+struct LutPlan {
+    int slices, tiles_per_block, row_blocks;
+};
+
+static LutPlan lut_plan(const Geometry& g, int k) {
+    LutPlan pl;
+    const int64_t n_slots = (int64_t)k * g.n_gt;
+    pl.slices = (int)((n_slots + LUT_SLOTS - 1) / LUT_SLOTS);
+    int64_t rb = LUT_CUS / pl.slices;
+    if (rb < 1) rb = 1;
+    if (rb > g.n_rt) rb = g.n_rt;
+    int64_t tpb = (g.n_rt + rb - 1) / rb;
+    if (tpb > LUT_WAVES * LUT_TILES_PER_WAVE) tpb = LUT_WAVES * LUT_TILES_PER_WAVE;
+    pl.tiles_per_block = (int)tpb;
+    pl.row_blocks = (int)((g.n_rt + tpb - 1) / tpb);
+    return pl;
+}
+
+static size_t acc_bytes(const Geometry& g) { return ((size_t)g.d_out * 8 + 255) / 256 * 256; }
+
+size_t gemv_lut_workspace_bytes(const Geometry& g) {
+    // one fixed-point accumulator per row, then one counter per row block (at most one per row tile)
+    return acc_bytes(g) + (size_t)g.n_rt * 4;
+}
+
+bool gemv_lut_supported(const Geometry& g, int batch) {
+    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && g.d_out < ((int64_t)1 << 31) / 2;
+}
+
+hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                           const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s) {
+    const LutPlan pl = lut_plan(g, k);
+    LutArgs a;
+    a.packed = packed;
+    a.codebooks = codebooks;
+    a.scales = scales;
+    a.x = x;
+    a.y = y;
+    a.acc = static_cast<unsigned long long*>(ws);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + acc_bytes(g));
+    a.d_out = g.d_out;
+    a.G = g.G;
+    a.n_rt = g.n_rt;
+    a.n_gt = g.n_gt;
+    a.plane_bytes = g.plane_bytes;
+    a.k = k;
+    a.n_slots = (int)((int64_t)k * g.n_gt);
+    a.slices = pl.slices;
+    a.tiles_per_block = pl.tiles_per_block;
+    const unsigned grid = (unsigned)(pl.slices * pl.row_blocks);
+    const dim3 gd(grid), bd(64 * LUT_WAVES);
+    switch (k) {
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1>), gd, bd, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2>), gd, bd, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3>), gd, bd, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4>), gd, bd, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5>), gd, bd, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6>), gd, bd, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7>), gd, bd, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8>), gd, bd, 0, s, a); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace aqd

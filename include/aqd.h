@@ -143,11 +143,13 @@ aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out
  * y:            fp16 [batch][d_out].
  * k:            1..M.  batch: 1..8.
  * workspace:    device scratch of aqd_gemv_workspace_bytes(layer, batch) bytes
- *               (may be NULL when that is 0).  It must be zero-filled before
- *               its first use; every successful call leaves it zero-filled
- *               again, so one buffer serves any number of calls on one stream
- *               (calls that overlap in time need separate workspaces).
- * Accumulation is fp32; the summation order is not specified.
+ *               (depends only on the layer; NULL allowed when it is 0).  It
+ *               must be zero-filled before its first use; every successful call
+ *               leaves the parts that must start at zero zeroed again, so one
+ *               buffer serves any number of calls on one stream.  Calls that
+ *               may overlap in time need separate workspaces.
+ * Accumulation is fp32; the summation order is not specified, but it is fixed:
+ * repeating a call on the same inputs gives the same bits.
  * packed_codes, x_rot and workspace 16-byte aligned; codebooks 16-byte aligned.
  * ------------------------------------------------------------------------- */
 size_t aqd_gemv_workspace_bytes(const aqd_layer* layer, int32_t batch);

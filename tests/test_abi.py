@@ -158,3 +158,11 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(aqd, "LIB_PATH", str(tmp_path / "libaqd.so"))
     with pytest.raises(RuntimeError, match="missing"):
         aqd.lib()
+
+
+def test_gemv_workspace_required(L):
+    need = L.aqd_gemv_workspace_bytes(lay(4096, 14336, 4), 1)
+    assert need >= 4 * 4096
+    assert _gemv(L, layer=lay(4096, 14336, 4), ws=None, ws_bytes=0) == E_WS
+    assert _gemv(L, layer=lay(4096, 14336, 4), ws=FAKE, ws_bytes=need - 1) == E_WS
+    assert _gemv(L, layer=lay(4096, 14336, 4), ws=FAKE_ODD, ws_bytes=need) == E_ALIGN

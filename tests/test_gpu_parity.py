@@ -284,3 +284,23 @@ def test_quantized_linear_forward(orc):
         y = q.forward(to_dev(x), 3).float().cpu().numpy()
         ref = orc.forward(codes, cb, s, 3, x, lin.block)
         assert normwise(y, ref) <= TOL, B
+
+
+def test_gemv_workspace_reusable_and_deterministic(orc):
+    """The batch-1 path keeps partials and counters in the workspace: its counters must be zero again after
+    every call (so one buffer serves the next call), and repeated calls must give the same bits."""
+    lin = wl.config(2)[0]
+    codes, cb, s, x = wl.layer_inputs(2, lin)
+    packed = aqd.aqd_pack_codes(to_dev(codes))
+    need = aqd.aqd_gemv_workspace_bytes(lin.d_out, lin.d_in, lin.M, 1)
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev())
+    xr = aqd.aqd_hadamard_rotate(to_dev(x), lin.block, aqd.AQD_F16)
+    outs = []
+    for k in (4, 1, 4, 2):
+        outs.append(aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), k, xr, lin.d_out, lin.d_in, 4, workspace=ws))
+        torch.cuda.synchronize()
+        counters = ws[-4 * ((lin.d_out + 15) // 16):]
+        assert torch.count_nonzero(counters).item() == 0, k
+    assert torch.equal(outs[0], outs[2])       # same inputs, same bits
+    ref = orc.forward(codes, cb, s, 2, x, lin.block)
+    assert normwise(outs[3].cpu().numpy(), ref) <= TOL
