@@ -55,7 +55,7 @@ size_t gemv_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
 size_t gemv_lut_workspace_bytes(const Geometry& g);
-bool gemv_lut_supported(const Geometry& g, int batch);
+bool gemv_lut_supported(const Geometry& g, int batch, int k);
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                            const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);

@@ -163,7 +163,7 @@ static hipError_t launch_nb(const uint8_t* packed, const uint16_t* cb, const uin
 
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
-    if (gemv_lut_supported(g, batch)) return launch_gemv_lut(packed, codebooks, scales, k, x, y, g, ws, s);
+    if (gemv_lut_supported(g, batch, k)) return launch_gemv_lut(packed, codebooks, scales, k, x, y, g, ws, s);
     switch (batch) {
         case 1: return launch_nb<1>(packed, codebooks, scales, k, x, y, g, s);
         case 2: return launch_nb<2>(packed, codebooks, scales, k, x, y, g, s);

@@ -26,13 +26,12 @@
 // Reduction.  Each lane holds 16 row partials (its group, all slots).  A
 // transposing butterfly (permlane32 swap, permlane16 swap, row mirror, half
 // row mirror, quad DPP) leaves row (l >> 2) summed over the wave in lane l.
-// Each slice adds its row sums to a per-row accumulator in the workspace as
-// 64-bit fixed point (device-scope integer atomics, so the total is exact and
-// independent of arrival order); the last workgroup of a row block to finish
-// (counted with an atomic counter) takes each total with one atomic exchange,
-// scales by s_i, rounds to fp16 and writes y.  The exchange and a counter reset
-// leave the workspace zero for the next call; results are reproducible bit for
-// bit.
+// Each slice adds its row sums into one 64-bit word per row in the workspace
+// (a contribution count plus a fixed-point sum, device-scope integer atomics);
+// the lane whose atomic add completes the count holds the exact total, scales
+// it by s_i, rounds to fp16, writes y and clears the word.  No barrier or
+// counter is needed, results are bit-reproducible, and the workspace is zero
+// again when the kernel ends.
 #include "aqd_internal.h"
 
 namespace aqd {
@@ -53,8 +52,7 @@ struct LutArgs {
     const uint16_t* scales;
     const uint16_t* x;
     uint16_t* y;
-    unsigned long long* acc;  // workspace: int64 [d_out] fixed-point row sums, zero between calls
-    uint32_t* counters;  // workspace: uint32 [row blocks], zero between calls
+    unsigned long long* acc;  // workspace: [d_out] counted fixed-point row sums, zero between calls
     int64_t d_out, G, n_rt, n_gt, plane_bytes;
     int k, n_slots, slices, tiles_per_block;
 };
@@ -72,19 +70,23 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t code_dword, uint32_t base,
     return __builtin_amdgcn_perm(code_dword, base, 0x0C020000u | ((uint32_t)(4 + byte) << 8));
 }
 
-// Row sums travel between workgroups as two's-complement fixed point with 32
-// fraction bits (|sum| < 2^31), so their total is exact and order independent.
-constexpr double FIX_ONE = 4294967296.0;  // 2^32
-constexpr double FIX_MAX = 2147483647.0 * 4294967296.0;
+// Row sums travel between workgroups in one 64-bit word per row: the top 8
+// bits count the contributions, the low 56 bits hold the sum of the
+// contributions as fixed point with 24 fraction bits, each biased by 2^47 so
+// that every term is non-negative and no carry reaches the count (at most 255
+// terms below 2^48 each).  Integer addition makes the total exact and
+// independent of arrival order; the adder that sees S-1 earlier contributions
+// in the returned word holds the complete sum.
+constexpr int FIX_FRAC = 24;
+constexpr int FIX_COUNT_SHIFT = 56;
+constexpr unsigned long long FIX_BIAS = 1ull << 47;
+constexpr double FIX_LIMIT = (double)((1ll << 47) - 1);
+constexpr int LUT_MAX_SLICES = 255;
 
-__device__ __forceinline__ unsigned long long to_fixed(float v) {
-    double d = (double)v * FIX_ONE;
-    d = d > FIX_MAX ? FIX_MAX : (d < -FIX_MAX ? -FIX_MAX : d);
-    return (unsigned long long)__double2ll_rn(d);
-}
-
-__device__ __forceinline__ float from_fixed(unsigned long long u) {
-    return (float)((double)(long long)u * (1.0 / FIX_ONE));
+__device__ __forceinline__ unsigned long long fix_term(float v) {
+    double d = (double)v * (double)(1 << FIX_FRAC);
+    d = d > FIX_LIMIT ? FIX_LIMIT : (d < -FIX_LIMIT ? -FIX_LIMIT : d);
+    return (unsigned long long)(__double2ll_rn(d) + (long long)FIX_BIAS);
 }
 
 template <int CTRL>
@@ -225,6 +227,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     for (int s = 0; s < LUT_SLOTS; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
     const half2_t ones = half2_t{(_Float16)1.0f, (_Float16)1.0f};
 
+    // returned accumulator words are examined only after the last tile, so the
+    // atomics' round trips overlap the remaining lookups
+    unsigned long long old_word[LUT_TILES_PER_WAVE], term[LUT_TILES_PER_WAVE];
+    bool mine[LUT_TILES_PER_WAVE];
+#pragma unroll
+    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+        mine[u] = false;
+        old_word[u] = 0ull;
+        term[u] = 0ull;
+    }
 #pragma unroll
     for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
@@ -243,36 +255,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
                 const uint32_t a1 = lut_addr(w1, base[2 * pr + 1], r & 3);
                 const half2_t v = half2_t{*reinterpret_cast<const _Float16*>(lds + a0),
                                           *reinterpret_cast<const _Float16*>(lds + a1)};
-                a = __builtin_amdgcn_fdot2(v, ones, a, false);
+                a = pr == 0 ? __builtin_amdgcn_fdot2(v, ones, 0.0f, false) : __builtin_amdgcn_fdot2(v, ones, a, false);
             }
             rows[r] = a;
         }
         const float sum = fold_rows(rows, lane);
         const int64_t row = it * TILE_ROWS + (lane >> 2);
-        if ((lane & 3) == 0 && row < p.d_out) atomicAdd(p.acc + row, to_fixed(sum));
-    }
-
-    // ---- the last slice to finish a row block writes it out.  Every slice's
-    // row sums were added as fixed-point integers, so the total does not depend
-    // on the order the slices arrive in.  Each wave waits until its atomics are
-    // performed before the counter is bumped; the last workgroup takes each row
-    // total with one exchange, which also clears the accumulator for the next call.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    uint32_t* flag = reinterpret_cast<uint32_t*>(lds + LUT_BYTES);
-    if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(p.counters + rb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *flag = (done == (uint32_t)(p.slices - 1)) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (*flag) {
-        const int64_t r0 = t0 * TILE_ROWS;
-        const int64_t r1 = t1 * TILE_ROWS < p.d_out ? t1 * TILE_ROWS : p.d_out;
-        for (int64_t i = r0 + tid; i < r1; i += 64 * WAVES) {
-            const unsigned long long t = atomicExch(p.acc + i, 0ull);
-            p.y[i] = f2h(h2f(p.scales[i]) * from_fixed(t));
+        if ((lane & 3) == 0 && row < p.d_out) {
+            mine[u] = true;
+            term[u] = fix_term(sum);
+            old_word[u] = atomicAdd(p.acc + row, (1ull << FIX_COUNT_SHIFT) + term[u]);
         }
-        if (tid == 0) __hip_atomic_store(p.counters + rb, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+        if (!mine[u] || (int)(old_word[u] >> FIX_COUNT_SHIFT) != p.slices - 1) continue;
+        // this lane added the last contribution of its row: it holds the complete sum
+        const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
+        if (row >= p.d_out) continue;
+        const unsigned long long biased = (old_word[u] & ((1ull << FIX_COUNT_SHIFT) - 1)) + term[u];
+        const long long total = (long long)biased - (long long)p.slices * (long long)FIX_BIAS;
+        p.y[row] = f2h(h2f(p.scales[row]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
+        __hip_atomic_store(p.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -298,13 +302,11 @@ static LutPlan lut_plan(const Geometry& g, int k) {
 
 static size_t acc_bytes(const Geometry& g) { return ((size_t)g.d_out * 8 + 255) / 256 * 256; }
 
-size_t gemv_lut_workspace_bytes(const Geometry& g) {
-    // one fixed-point accumulator per row, then one counter per row block (at most one per row tile)
-    return acc_bytes(g) + (size_t)g.n_rt * 4;
-}
+size_t gemv_lut_workspace_bytes(const Geometry& g) { return acc_bytes(g); }
 
-bool gemv_lut_supported(const Geometry& g, int batch) {
-    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && g.d_out < ((int64_t)1 << 31) / 2;
+bool gemv_lut_supported(const Geometry& g, int batch, int k) {
+    const int64_t slices = ((int64_t)k * g.n_gt + LUT_SLOTS - 1) / LUT_SLOTS;
+    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && slices <= LUT_MAX_SLICES;
 }
 
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
@@ -317,7 +319,6 @@ hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, con
     a.x = x;
     a.y = y;
     a.acc = static_cast<unsigned long long*>(ws);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + acc_bytes(g));
     a.d_out = g.d_out;
     a.G = g.G;
     a.n_rt = g.n_rt;

@@ -299,8 +299,7 @@ def test_gemv_workspace_reusable_and_deterministic(orc):
     for k in (4, 1, 4, 2):
         outs.append(aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), k, xr, lin.d_out, lin.d_in, 4, workspace=ws))
         torch.cuda.synchronize()
-        counters = ws[-4 * ((lin.d_out + 15) // 16):]
-        assert torch.count_nonzero(counters).item() == 0, k
+        assert torch.count_nonzero(ws).item() == 0, k
     assert torch.equal(outs[0], outs[2])       # same inputs, same bits
     ref = orc.forward(codes, cb, s, 2, x, lin.block)
     assert normwise(outs[3].cpu().numpy(), ref) <= TOL
