@@ -161,7 +161,8 @@ def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: 
                          x_rot: torch.Tensor, d_out: int, d_in: int, M: int, x_dtype: int = AQD_BF16X2,
                          out: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y[batch][d_out] fp32 for x_rot bf16 [batch][d_in] (AQD_BF16) or [2][batch][d_in] (AQD_BF16X2)."""
+    """y[batch][d_out] fp32 for x_rot bf16 [batch][d_in] (AQD_BF16), [2][batch][d_in] (AQD_BF16X2) or
+    fp16 [batch][d_in] (AQD_F16)."""
     batch = x_rot.shape[-2]
     L = layer(d_out, d_in, M)
     if out is None:
@@ -179,8 +180,8 @@ class QuantizedLinear:
     """One additive-codebook linear resident on the GPU: packed codes, codebooks, scales.
 
     ``forward(x, k)`` rotates the activation online and applies the k-codebook
-    product: batch 1..8 through the GEMV, larger batches through the bf16
-    matrix-core path (fp32 output).
+    product: batch 1..8 through the GEMV (fp16 output), batch 9..64 through the
+    fp16 matrix-core path (fp32 output).
     """
 
     def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, block: int):
@@ -190,8 +191,8 @@ class QuantizedLinear:
         self.codebooks = codebooks.contiguous()
         self.scales = scales.contiguous()
         self.workspace = None
-        n = max(aqd_gemv_workspace_bytes(d_out, self.d_in, M, 8),
-                aqd_gemm_small_batch_workspace_bytes(d_out, self.d_in, M, 64))
+        n = max([aqd_gemv_workspace_bytes(d_out, self.d_in, M, b) for b in range(1, 9)] +
+                [aqd_gemm_small_batch_workspace_bytes(d_out, self.d_in, M, b) for b in range(9, 65)])
         if n:
             self.workspace = torch.zeros(n, dtype=torch.uint8, device=codes.device)
 
@@ -201,6 +202,6 @@ class QuantizedLinear:
             xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
             return aqd_gemv(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
                             workspace=self.workspace)
-        xr = aqd_hadamard_rotate(x2, self.block, AQD_BF16X2)
+        xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
         return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
-                                    AQD_BF16X2, workspace=self.workspace)
+                                    AQD_F16, workspace=self.workspace)

@@ -158,14 +158,14 @@ aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* cod
                                 int32_t k, const void* x_rot, int x_dtype, float* y, int32_t batch,
                                 const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream) {
     if (batch < 1 || batch > 64) return fail(AQD_ERR_SHAPE, "aqd_gemm_small_batch batch must be in [1, 64]");
-    if (x_dtype != AQD_BF16 && x_dtype != AQD_BF16X2)
-        return fail(AQD_ERR_DTYPE, "x_dtype must be BF16 or BF16X2");
+    if (x_dtype != AQD_F16 && x_dtype != AQD_BF16 && x_dtype != AQD_BF16X2)
+        return fail(AQD_ERR_DTYPE, "x_dtype must be F16, BF16 or BF16X2");
     bool nothing = false;
     size_t need = layer ? aqd_gemm_small_batch_workspace_bytes(layer, batch) : 0;
     aqd_status st = check_product(packed_codes, codebooks, scales, k, x_rot, y, layer, workspace,
                                   workspace_bytes, need, &nothing);
     if (st != AQD_OK || nothing) return st;
-    if (!aligned16(y)) return fail(AQD_ERR_ALIGN, "y must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(y) % 4) return fail(AQD_ERR_ALIGN, "y must be 4-byte aligned");
     return hip_status(launch_gemm_sb(packed_codes, codebooks, scales, k, x_rot, x_dtype, y, batch,
                                      geometry(*layer), workspace, (hipStream_t)stream),
                       "aqd_gemm_small_batch");

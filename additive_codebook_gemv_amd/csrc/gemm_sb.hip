@@ -1,118 +1,212 @@
-// Small-batch product (batch 1..64) on the bf16 matrix cores.
+// Small-batch product (batch 1..64) on the matrix cores.
 //
-// Same operation as the GEMV (Drop-by-Drop, section 3.2 reconstruction from
-// the first k codebooks, section 5), but with enough activation columns that
-// the work is a dense contraction: each wave rebuilds a 16-row x 32-input
-// slice of the weights from the codes (codeword sums in fp32), splits it into
-// bf16 hi + lo, and feeds it to v_mfma_f32_16x16x32_bf16 against 16-column
-// tiles of the rotated activation, accumulating in fp32.
+// Same operation as the GEMV (Drop-by-Drop, section 3.2: a weight group is the
+// sum of the codewords its codes pick; section 5: only the first k codebooks),
+// but with enough activation columns that the work is a dense contraction:
+//     Y[n][i] = s_i * sum_c W_k[i][c] * X[n][c].
 //
-// Workgroup: 4 waves, one 16-row tile each; the k codebooks live in LDS and the
-// code tiles of the current group tile are staged in LDS so that each lane can
-// pick the codes of exactly the weights its MFMA operand slot holds.  The
-// group tiles are split over gridDim.y; partial results are added atomically
-// into y (zero-filled first) when the split is more than one.
+// Workgroup: 8 waves, one 16-row tile each (128 rows), all batch columns, a
+// range of 128-input chunks (the input dimension is split over gridDim.y).
+// Per chunk:
+//   - the rotated activation chunk (batch x 128) is staged once in LDS, double
+//     buffered, and shared by the 8 waves (MFMA B operands, padded rows so the
+//     16-byte reads do not collide);
+//   - each lane rebuilds exactly the 8 weights its MFMA A-operand slot holds:
+//     it gathers the k codewords of its (row, group) from the LDS-resident
+//     codebooks and adds them with packed fp16 adds;
+//   - v_mfma_f32_16x16x32 multiplies the 16x32 weight slice by every 16-column
+//     tile of the activation, accumulating in fp32.
+// Precision modes: AQD_F16 activations use one fp16 MFMA pass (weights are the
+// fp16 codeword sums); AQD_BF16 splits the weights into bf16 hi + lo (two
+// passes); AQD_BF16X2 also adds the activation's lo plane (three passes).
+// Split inputs: each split writes its partial rows to the workspace and a
+// second kernel adds the splits in a fixed order, scales and stores Y, so the
+// result is bit-reproducible.
 #include "aqd_internal.h"
 
 namespace aqd {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int SB_WAVES = 4;
+constexpr int SB_WAVES = 8;
+constexpr int SB_CHUNK = 128;                      // inputs per chunk (16 groups)
+constexpr int SB_CHUNK_GROUPS = SB_CHUNK / GROUP;
+constexpr int SB_XROW = SB_CHUNK * 2 + 16;         // bytes per activation row in LDS (padded)
+constexpr int SB_MAX_SPLITS = 16;
 
-__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = 0.f;
+template <int MODE>
+struct XPlanes {
+    static constexpr int n = MODE == AQD_BF16X2 ? 2 : 1;
+};
+
+__device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// fp16 pair -> bf16 hi pair and bf16 lo pair (hi + lo equals the pair to 2^-16)
+__device__ __forceinline__ void split_bf16(uint32_t h, uint32_t& hi, uint32_t& lo) {
+    const half2_t v = h2(h);
+    const float a = (float)v[0], b = (float)v[1];
+    const uint32_t ha = f2bf(a), hb = f2bf(b);
+    const uint32_t la = f2bf(a - bf2f((uint16_t)ha)), lb = f2bf(b - bf2f((uint16_t)hb));
+    hi = ha | (hb << 16);
+    lo = la | (lb << 16);
 }
 
-__device__ __forceinline__ void add_codeword(float (&w)[8], const uint4& c) {
-    const uint32_t u[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        w[2 * q] += h2f((uint16_t)(u[q] & 0xFFFFu));
-        w[2 * q + 1] += h2f((uint16_t)(u[q] >> 16));
-    }
-}
-
-template <int NT, bool XLO>
+template <int NT, int MODE, int K>
 __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     const uint8_t* __restrict__ packed, const uint4* __restrict__ codebooks, const uint16_t* __restrict__ scales,
-    int k, const uint16_t* __restrict__ x, float* __restrict__ y, int64_t d_out, int64_t d_in, int64_t G,
-    int64_t n_rt, int64_t n_gt, int64_t plane_bytes, int batch, int64_t gt_per_split, int atomic) {
-    extern __shared__ uint4 lds[];
-    uint4* cb_lds = lds;                                               // [k][256]
-    uint8_t* tiles = reinterpret_cast<uint8_t*>(lds + k * CODEWORDS);  // [wave][k][1024]
+    const uint16_t* __restrict__ x, float* __restrict__ out, int64_t d_out, int64_t d_in, int64_t G,
+    int64_t n_rt, int64_t plane_bytes, int batch, int chunks_per_split, int64_t n_chunks, int direct) {
+    constexpr int XP = XPlanes<MODE>::n;
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint4* cb_lds = reinterpret_cast<uint4*>(lds);                        // [k][256] codewords
+    uint8_t* xbuf = lds + K * CODEWORDS * 16;                             // [2][XP][NT*16][SB_XROW]
+    constexpr int XBUF = XP * NT * 16 * SB_XROW;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t it = (int64_t)blockIdx.x * SB_WAVES + wave;
+    const int64_t it = (int64_t)blockIdx.x * SB_WAVES + wave;            // this wave's row tile
     const bool row_ok = it < n_rt;
-    const int64_t gt0 = (int64_t)blockIdx.y * gt_per_split;
-    const int64_t gt1 = gt0 + gt_per_split < n_gt ? gt0 + gt_per_split : n_gt;
+    const int64_t c0 = (int64_t)blockIdx.y * chunks_per_split;
+    const int64_t c1 = c0 + chunks_per_split < n_chunks ? c0 + chunks_per_split : n_chunks;
+    const int r = lane & 15;      // MFMA A row (weight row in the tile) / B column in the tile
+    const int kq = lane >> 4;     // 8-wide k slot inside the 32-wide MFMA step
 
-    for (int i = tid; i < k * CODEWORDS; i += 64 * SB_WAVES) cb_lds[i] = codebooks[i];
+    for (int i = tid; i < K * CODEWORDS; i += 64 * SB_WAVES) cb_lds[i] = codebooks[i];
+
+    // activation chunk staging: thread t moves 16 bytes (8 inputs) of one row of one plane
+    constexpr int X_ITEMS = XP * NT * 16 * (SB_CHUNK / 8);   // 16-byte pieces per chunk
+    constexpr int X_PER_THREAD = (X_ITEMS + 64 * SB_WAVES - 1) / (64 * SB_WAVES);
+    // every load is issued unconditionally (addresses clamped into the buffer, out-of-range pieces zeroed
+    // afterwards), so the loads of the next chunk stay in flight while this chunk is multiplied
+    auto x_load = [&](int64_t ch, uint4 (&v)[X_PER_THREAD]) {
+#pragma unroll
+        for (int q = 0; q < X_PER_THREAD; ++q) {
+            const int item = (tid + q * 64 * SB_WAVES) % X_ITEMS;
+            const int piece = item % (SB_CHUNK / 8);
+            const int col = (item / (SB_CHUNK / 8)) % (NT * 16);
+            const int pl = item / ((SB_CHUNK / 8) * NT * 16);
+            const int64_t kk = ch * SB_CHUNK + piece * 8;
+            const int colc = col < batch ? col : batch - 1;
+            const int64_t kkc = kk < d_in ? kk : d_in - 8;
+            v[q] = *reinterpret_cast<const uint4*>(x + (int64_t)pl * batch * d_in + (int64_t)colc * d_in + kkc);
+        }
+    };
+    auto x_fix = [&](int64_t ch, uint4 (&v)[X_PER_THREAD]) {
+#pragma unroll
+        for (int q = 0; q < X_PER_THREAD; ++q) {
+            const int item = (tid + q * 64 * SB_WAVES) % X_ITEMS;
+            const int piece = item % (SB_CHUNK / 8);
+            const int col = (item / (SB_CHUNK / 8)) % (NT * 16);
+            if (col >= batch || ch * SB_CHUNK + piece * 8 >= d_in) v[q] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto x_store = [&](int buf, const uint4 (&v)[X_PER_THREAD]) {
+#pragma unroll
+        for (int q = 0; q < X_PER_THREAD; ++q) {
+            const int item = tid + q * 64 * SB_WAVES;
+            if (item < X_ITEMS) {
+                const int piece = item % (SB_CHUNK / 8);
+                const int row = item / (SB_CHUNK / 8);          // pl * NT*16 + col
+                *reinterpret_cast<uint4*>(xbuf + buf * XBUF + row * SB_XROW + piece * 16) = v[q];
+            }
+        }
+    };
+    // code bytes of this wave for one chunk: lane l needs, per plane and per 32-input step s,
+    // the code of row r, group 4s + kq; inside a tile those 64 bytes are contiguous
+    auto code_load = [&](int64_t ch, uint32_t (&cv)[K][4]) {
+        const int64_t jt = (ch * SB_CHUNK_GROUPS) / TILE_GROUPS;
+        const int g0 = (int)((ch * SB_CHUNK_GROUPS) % TILE_GROUPS);
+        const int64_t itc = row_ok ? it : 0;
+        const uint8_t* base = packed + (jt * n_rt + itc) * TILE_BYTES + g0 * TILE_ROWS + lane;
+#pragma unroll
+        for (int m = 0; m < K; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cv[m][s] = base[m * plane_bytes + 4 * s * TILE_ROWS];
+    };
 
     floatx4_t acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    uint8_t* my_tiles = tiles + (size_t)wave * k * TILE_BYTES;
-    const uint16_t* x_lo = x + (int64_t)batch * d_in;
-    const int r = lane & 15;     // weight row inside the tile (MFMA A row)
-    const int kq = lane >> 4;    // which 8-wide k slot of the 32-wide MFMA step
-
-    for (int64_t jt = gt0; jt < gt1; ++jt) {
-        __syncthreads();  // previous tiles consumed (and codebooks stored on the first pass)
-        if (row_ok) {
-            for (int m = 0; m < k; ++m) {
-                const uint4 v = *reinterpret_cast<const uint4*>(packed + m * plane_bytes +
-                                                                (jt * n_rt + it) * TILE_BYTES + lane * TILE_ROWS);
-                *reinterpret_cast<uint4*>(my_tiles + m * TILE_BYTES + lane * TILE_ROWS) = v;
-            }
+    uint4 xv[X_PER_THREAD];
+    uint32_t cv[K][4];
+    if (c0 < c1) {
+        x_load(c0, xv);
+        code_load(c0, cv);
+        x_fix(c0, xv);
+        x_store(0, xv);
+    }
+    int buf = 0;
+    for (int64_t ch = c0; ch < c1; ++ch) {
+        __syncthreads();                      // chunk `ch` is in xbuf[buf]; codebooks are in LDS
+        uint32_t cur[K][4];
+#pragma unroll
+        for (int m = 0; m < K; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) cur[m][s] = cv[m][s];
+        if (ch + 1 < c1) {                    // prefetch the next chunk while this one is multiplied
+            x_load(ch + 1, xv);
+            code_load(ch + 1, cv);
         }
-        __syncthreads();
-        if (!row_ok) continue;
-#pragma unroll 2
-        for (int s = 0; s < TILE_GROUPS / 4; ++s) {
-            const int gl = 4 * s + kq;
-            const int64_t j = jt * TILE_GROUPS + gl;
-            float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const uint8_t* xb = xbuf + buf * XBUF;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int64_t j = ch * SB_CHUNK_GROUPS + 4 * s + kq;   // this lane's group
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
             if (j < G) {
-                for (int m = 0; m < k; ++m) {
-                    const uint32_t c = my_tiles[m * TILE_BYTES + gl * TILE_ROWS + r];
-                    add_codeword(w, cb_lds[m * CODEWORDS + c]);
+#pragma unroll
+                for (int m = 0; m < K; ++m) {
+                    const uint4 c = cb_lds[m * CODEWORDS + cur[m][s]];
+                    if (m == 0) {
+                        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+                    } else {
+                        w[0] = u32(h2(w[0]) + h2(c.x));
+                        w[1] = u32(h2(w[1]) + h2(c.y));
+                        w[2] = u32(h2(w[2]) + h2(c.z));
+                        w[3] = u32(h2(w[3]) + h2(c.w));
+                    }
                 }
             }
-            bf16x8_t a_hi, a_lo;
+            const int kofs = (32 * s + 8 * kq) * 2;
+            if (MODE == AQD_F16) {
+                const half8_t a = __builtin_bit_cast(half8_t, make_uint4(w[0], w[1], w[2], w[3]));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 h = (__bf16)w[e];
-                a_hi[e] = h;
-                a_lo[e] = (__bf16)(w[e] - (float)h);
-            }
-            const int64_t kk = j * GROUP;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int col = t * 16 + r;
-                uint4 bh = {0u, 0u, 0u, 0u}, bl = {0u, 0u, 0u, 0u};
-                if (col < batch && j < G) {
-                    bh = *reinterpret_cast<const uint4*>(x + (int64_t)col * d_in + kk);
-                    if (XLO) bl = *reinterpret_cast<const uint4*>(x_lo + (int64_t)col * d_in + kk);
+                for (int t = 0; t < NT; ++t) {
+                    const uint4 bx = *reinterpret_cast<const uint4*>(xb + (t * 16 + r) * SB_XROW + kofs);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, bx), acc[t], 0, 0, 0);
                 }
-                const bf16x8_t b_hi = __builtin_bit_cast(bf16x8_t, bh);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_hi, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b_hi, acc[t], 0, 0, 0);
-                if (XLO) {
-                    const bf16x8_t b_lo = __builtin_bit_cast(bf16x8_t, bl);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b_lo, acc[t], 0, 0, 0);
+            } else {
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) split_bf16(w[q], hi[q], lo[q]);
+                const bf16x8_t ahi = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                const bf16x8_t alo = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint4 bh = *reinterpret_cast<const uint4*>(xb + (t * 16 + r) * SB_XROW + kofs);
+                    const bf16x8_t bhi = __builtin_bit_cast(bf16x8_t, bh);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, bhi, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo, bhi, acc[t], 0, 0, 0);
+                    if (MODE == AQD_BF16X2) {
+                        const uint4 bl = *reinterpret_cast<const uint4*>(xb + ((NT + t) * 16 + r) * SB_XROW + kofs);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi, __builtin_bit_cast(bf16x8_t, bl), acc[t], 0, 0, 0);
+                    }
                 }
             }
         }
+        if (ch + 1 < c1) {                    // the other buffer was last read before this chunk's barrier
+            x_fix(ch + 1, xv);
+            x_store(buf ^ 1, xv);
+        }
+        buf ^= 1;
     }
 
     if (!row_ok) return;
+    // lane l holds rows 4*kq .. 4*kq+3 of the tile, column t*16 + r
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         const int col = t * 16 + r;
@@ -121,56 +215,151 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
         for (int q = 0; q < 4; ++q) {
             const int64_t i = it * TILE_ROWS + 4 * kq + q;
             if (i >= d_out) continue;
-            const float v = h2f(scales[i]) * acc[t][q];
-            if (atomic) unsafeAtomicAdd(y + (int64_t)col * d_out + i, v);
-            else y[(int64_t)col * d_out + i] = v;
+            if (direct) out[(int64_t)col * d_out + i] = h2f(scales[i]) * acc[t][q];
+            else out[((int64_t)blockIdx.y * batch + col) * d_out + i] = acc[t][q];
         }
     }
 }
 
-size_t gemm_sb_workspace_bytes(const Geometry&, int) { return 0; }
-
-template <int NT, bool XLO>
-static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
-                           const uint16_t* x, float* y, int batch, const Geometry& g, hipStream_t s) {
-    const int64_t wg_rows = (g.n_rt + SB_WAVES - 1) / SB_WAVES;
-    int64_t splits = (512 + wg_rows - 1) / wg_rows;
-    if (splits > g.n_gt) splits = g.n_gt;
-    if (splits > 16) splits = 16;
-    if (splits < 1) splits = 1;
-    const int64_t per = g.n_gt > 0 ? (g.n_gt + splits - 1) / splits : 0;
-    if (per > 0) splits = (g.n_gt + per - 1) / per;
-    const int atomic = splits > 1 ? 1 : 0;
-    if (atomic || g.n_gt == 0) {
-        const int64_t n = (int64_t)batch * g.d_out;
-        hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
-                           dim3(256), 0, s, y, n);
-        if (g.n_gt == 0) return hipGetLastError();
+// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i]
+__global__ void sb_reduce_kernel(const float* __restrict__ part, const uint16_t* __restrict__ scales,
+                                 float* __restrict__ y, int64_t d_out, int batch, int splits) {
+    const int64_t n = (int64_t)batch * d_out;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        float v = 0.f;
+        for (int sp = 0; sp < splits; ++sp) v += part[(int64_t)sp * n + e];
+        y[e] = h2f(scales[e % d_out]) * v;
     }
-    const size_t lds = (size_t)k * CODEWORDS * 16 + (size_t)SB_WAVES * k * TILE_BYTES;
-    hipLaunchKernelGGL((gemm_sb_kernel<NT, XLO>), dim3((unsigned)wg_rows, (unsigned)splits), dim3(64 * SB_WAVES),
-                       lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, k, x, y, g.d_out, g.d_in, g.G,
-                       g.n_rt, g.n_gt, g.plane_bytes, batch, per, atomic);
+}
+
+__global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+        y[e] = 0.f;
+}
+
+template <int MODE>
+constexpr size_t sb_lds_bytes(int k, int nt) {
+    return (size_t)k * CODEWORDS * 16 + 2 * (size_t)XPlanes<MODE>::n * nt * 16 * SB_XROW;
+}
+
+struct SbPlan {
+    int64_t n_chunks, wg_rows;
+    int splits, chunks_per_split;
+};
+
+// Splits of the input dimension: the smallest split count that minimises
+// (rounds of workgroups over the chip) x (chunks per split), with `per_cu`
+// workgroups resident per compute unit; at most SB_MAX_SPLITS.
+static SbPlan sb_plan(const Geometry& g, int per_cu) {
+    SbPlan p;
+    p.n_chunks = (g.d_in + SB_CHUNK - 1) / SB_CHUNK;
+    p.wg_rows = (g.n_rt + SB_WAVES - 1) / SB_WAVES;
+    p.splits = 1;
+    p.chunks_per_split = (int)p.n_chunks;
+    if (p.wg_rows == 0 || p.n_chunks == 0) return p;
+    const int64_t slots = 256 * (int64_t)per_cu;
+    int64_t best = -1;
+    for (int64_t sp = 1; sp <= SB_MAX_SPLITS && sp <= p.n_chunks; ++sp) {
+        const int64_t cps = (p.n_chunks + sp - 1) / sp;
+        const int64_t used = (p.n_chunks + cps - 1) / cps;          // splits that actually hold chunks
+        const int64_t cost = ((p.wg_rows * used + slots - 1) / slots) * cps;
+        if (best < 0 || cost < best) {
+            best = cost;
+            p.splits = (int)used;
+            p.chunks_per_split = (int)cps;
+        }
+    }
+    return p;
+}
+
+// Workgroups of 8 waves resident per CU: bounded by the LDS the batch tile needs
+// (VGPR use, about 128 per lane, allows two).
+template <int MODE>
+static int sb_per_cu(int k, int batch) {
+    const size_t lds = sb_lds_bytes<MODE>(k, (batch + 15) / 16);
+    const int by_lds = (int)((160 * 1024) / lds);
+    return by_lds < 2 ? (by_lds < 1 ? 1 : by_lds) : 2;
+}
+
+static SbPlan sb_plan_for(const Geometry& g, int k, int batch, int x_dt) {
+    const int per_cu = x_dt == AQD_BF16X2 ? sb_per_cu<AQD_BF16X2>(k, batch) : sb_per_cu<AQD_F16>(k, batch);
+    return sb_plan(g, per_cu);
+}
+
+size_t gemm_sb_workspace_bytes(const Geometry& g, int batch) {
+    // the largest the plan can ask for over k and the operand modes
+    size_t need = 0;
+    for (int k = 1; k <= g.M && k <= MAX_M; ++k)
+        for (int dt : {AQD_F16, AQD_BF16X2}) {
+            const SbPlan p = sb_plan_for(g, k, batch, dt);
+            if (p.splits > 1) {
+                const size_t b = (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4;
+                need = b > need ? b : need;
+            }
+        }
+    return need;
+}
+
+template <int NT, int MODE, int K>
+static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+    const SbPlan p = sb_plan(g, sb_per_cu<MODE>(K, batch));
+    const int64_t n = (int64_t)batch * g.d_out;
+    if (p.n_chunks == 0) {                                   // empty input: Y = 0
+        hipLaunchKernelGGL(sb_zero_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
+                           dim3(256), 0, s, y, n);
+        return hipGetLastError();
+    }
+    const bool direct = p.splits == 1;
+    constexpr size_t lds = sb_lds_bytes<MODE>(K, NT);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)lds);
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL((gemm_sb_kernel<NT, MODE, K>), dim3((unsigned)p.wg_rows, (unsigned)p.splits),
+                       dim3(64 * SB_WAVES), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
+                       direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
+                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || direct) return e;
+    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192)),
+                       dim3(256), 0, s, static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits);
     return hipGetLastError();
 }
 
-template <bool XLO>
-static hipError_t launch_x(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
-                           const uint16_t* x, float* y, int batch, const Geometry& g, hipStream_t s) {
-    const int nt = (batch + 15) / 16;
-    switch (nt) {
-        case 1: return launch_t<1, XLO>(packed, cb, scales, k, x, y, batch, g, s);
-        case 2: return launch_t<2, XLO>(packed, cb, scales, k, x, y, batch, g, s);
-        case 3: return launch_t<3, XLO>(packed, cb, scales, k, x, y, batch, g, s);
-        default: return launch_t<4, XLO>(packed, cb, scales, k, x, y, batch, g, s);
+template <int MODE, int K>
+static hipError_t launch_n(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+    switch ((batch + 15) / 16) {
+        case 1: return launch_t<1, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 2: return launch_t<2, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 3: return launch_t<3, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
+        default: return launch_t<4, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
+    }
+}
+
+template <int MODE>
+static hipError_t launch_m(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+    switch (k) {
+        case 1: return launch_n<MODE, 1>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 2: return launch_n<MODE, 2>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 3: return launch_n<MODE, 3>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 4: return launch_n<MODE, 4>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 5: return launch_n<MODE, 5>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 6: return launch_n<MODE, 6>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 7: return launch_n<MODE, 7>(packed, cb, scales, x, y, batch, g, ws, s);
+        default: return launch_n<MODE, 8>(packed, cb, scales, x, y, batch, g, ws, s);
     }
 }
 
 hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
-                          const void* x, int x_dt, float* y, int batch, const Geometry& g, void*, hipStream_t s) {
+                          const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,
+                          hipStream_t s) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (x_dt == AQD_BF16X2) return launch_x<true>(packed, codebooks, scales, k, xb, y, batch, g, s);
-    return launch_x<false>(packed, codebooks, scales, k, xb, y, batch, g, s);
+    if (x_dt == AQD_F16) return launch_m<AQD_F16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
+    if (x_dt == AQD_BF16X2) return launch_m<AQD_BF16X2>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
+    return launch_m<AQD_BF16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
 }
 
 }  // namespace aqd

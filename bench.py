@@ -13,8 +13,11 @@ in HBM before timing starts.
 Reported (one JSON line): mean microseconds per GEMV over the four bitwidths
 (`value`), per-k timings and HBM-roofline fractions, a roofline object for the
 k = 4 GEMV kernel (algorithmic bytes per launch / average launch time measured
-with HIP events on the launch stream), graph-captured sustained back-to-back
-rates, and the CPU oracle timed on the host cores on a bounded sample.
+with HIP events on the launch stream around a graph of K back-to-back
+launches), the same launches issued eagerly from Python, the 32-layer stack
+latency, the small-batch matrix-core path, and the CPU oracle timed on the host
+cores on a bounded sample (which also checks the GPU outputs of the timed
+configuration).
 """
 from __future__ import annotations
 
@@ -45,24 +48,31 @@ def code_bytes(k: int) -> int:
     return k * D_OUT * (D_IN // 8)
 
 
-def cpu_baseline(codes, cb, s, x, budget_s: float):
-    """The fp64 oracle on the host cores: full-size GEMVs (rotation included), k = 1..4 round-robin."""
+def cpu_baseline(codes, cb, s, x, budget_s: float, y_gpu=None):
+    """The fp64 oracle on the host cores: full-size GEMVs (rotation included), k = 1..4 round-robin.
+
+    Its first output per k is also compared with the GPU result of the timed configuration (normwise
+    max relative error), so the baseline and the measured kernels are seen to compute the same thing.
+    """
     import oracle
     orc = oracle.load()
     want = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
     threads = orc.set_threads(want)
     times = {k: [] for k in KS}
+    worst = 0.0
     t_start = time.perf_counter()
     while True:
         for k in KS:
             t0 = time.perf_counter()
-            orc.forward(codes, cb, s, k, x, BLOCK)
+            ref = orc.forward(codes, cb, s, k, x, BLOCK)
             times[k].append(time.perf_counter() - t0)
+            if y_gpu is not None and len(times[k]) == 1:
+                worst = max(worst, float(np.max(np.abs(y_gpu[k].astype(np.float64) - ref)) / np.max(np.abs(ref))))
         if time.perf_counter() - t_start >= budget_s:
             break
     per_k = {k: float(np.median(v)) * 1e6 for k, v in times.items()}
     reps = len(times[1])
-    return {
+    out = {
         "value": float(np.mean(list(per_k.values()))),
         "unit": "us per GEMV",
         "cores": threads,
@@ -71,6 +81,136 @@ def cpu_baseline(codes, cb, s, x, budget_s: float):
                   f"per k in 1..4, median per k, {time.perf_counter() - t_start:.1f} s of CPU work",
         "per_k_us": {str(k): v for k, v in per_k.items()},
     }
+    if y_gpu is not None:
+        out["gpu_vs_oracle_worst_err"] = worst
+        assert worst <= 2e-3, f"GPU output of the timed configuration disagrees with the oracle: {worst}"
+    return out
+
+
+def measure_stack(aqd, wl, torch, dev, replays: int = 20):
+    """One decode token through the synthetic 32-layer stack of 8B shape (linears and rotations only).
+
+    Per layer: q/k/v share one rotated input, o, gate/up (shared) and down get their own; every linear
+    uses the layer's seeded k.  The 352 launches of a token are captured in one graph and replayed.
+    """
+    lins = wl.config(4)
+    ks = wl.stack_ks()
+    layers = []
+    code_bytes = 0
+    for lin in lins:
+        codes, cb, sc, _ = wl.layer_inputs(4, lin)
+        packed = aqd.aqd_pack_codes(torch.from_numpy(codes).to(dev))
+        layers.append((lin, packed, torch.from_numpy(cb).to(dev), torch.from_numpy(sc).to(dev)))
+        code_bytes += lin.ks[0] * lin.d_out * (lin.d_in // 8)
+        del codes
+    ws_need = max(aqd.aqd_gemv_workspace_bytes(l.d_out, l.d_in, l.M, 1) for l in lins)
+    ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)
+    g = np.random.Generator(np.random.PCG64(0xA0D00004))
+    inputs = {}
+    for layer in range(32):
+        for name, d_in in (("qkv", 4096), ("o", 4096), ("mlp", 4096), ("down", 14336)):
+            x = g.standard_normal((1, d_in)).astype(np.float16)
+            inputs[(layer, name)] = (torch.from_numpy(x).to(dev), torch.empty((1, d_in), dtype=torch.float16, device=dev))
+    outs = [torch.empty((1, l.d_out), dtype=torch.float16, device=dev) for l in lins]
+    src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
+
+    def token():
+        for layer in range(32):
+            for name in ("qkv", "o", "mlp", "down"):
+                x, xr = inputs[(layer, name)]
+                aqd.aqd_hadamard_rotate(x, wl.block_for(x.shape[1]), aqd.AQD_F16, out=xr)
+            for j in range(7):
+                lin, packed, cb, sc = layers[layer * 7 + j]
+                xr = inputs[(layer, src[lin.proj])][1]
+                aqd.aqd_gemv(packed, cb, sc, lin.ks[0], xr, lin.d_out, lin.d_in, lin.M, out=outs[layer * 7 + j],
+                             workspace=ws)
+
+    stream = torch.cuda.current_stream()
+    token()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            token()
+    stream.wait_stream(side)
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / replays
+    a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a2.record(stream)
+    for _ in range(3):
+        token()
+    b2.record(stream)
+    torch.cuda.synchronize()
+    us_eager = a2.elapsed_time(b2) * 1e3 / 3
+    return {
+        "workload": "32-layer decoder stack of 8B shape (q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; "
+                    "down 4096x14336), batch 1, M=4, per-layer k from {2,3,4} (seeded), 4 rotations + 7 GEMVs "
+                    "per layer, linears and rotations only",
+        "layer_k": ks,
+        "launches_per_token": 32 * 11,
+        "code_bytes_per_token": code_bytes,
+        "us_per_token_graph": us,
+        "tokens_per_s_graph": 1e6 / us,
+        "us_per_token_eager": us_eager,
+        "frac_hbm_peak_graph": code_bytes / us / 1e3 / HBM_PEAK_GBPS,
+    }
+
+
+def measure_small_batch(aqd, wl, torch, dev, copies: int = 32, reps: int = 2):
+    """The matrix-core path on the 14336x4096 and 4096x14336 shapes at batch 16/32/64, k = 4 and 2, with
+    the activation as bf16 hi/lo planes (three bf16 passes) and as fp16 (one pass)."""
+    res = []
+    for lin in wl.config(5):
+        codes, cb, sc, _ = wl.layer_inputs(5, lin, batch=64)
+        packed0 = aqd.aqd_pack_codes(torch.from_numpy(codes).to(dev))
+        cps = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+        cbd, sd = torch.from_numpy(cb).to(dev), torch.from_numpy(sc).to(dev)
+        g = np.random.Generator(np.random.PCG64(0x5B))
+        x = torch.from_numpy(g.standard_normal((64, lin.d_in)).astype(np.float32)).to(dev).to(torch.bfloat16)
+        xr = {"bf16x2": aqd.aqd_hadamard_rotate(x, lin.block, aqd.AQD_BF16X2),
+              "f16": aqd.aqd_hadamard_rotate(x, lin.block, aqd.AQD_F16)}
+        dts = {"bf16x2": aqd.AQD_BF16X2, "f16": aqd.AQD_F16}
+        for mode in ("f16", "bf16x2"):
+            for k in lin.ks:
+                for B in lin.batches:
+                    xb = xr[mode][..., :B, :].contiguous()
+                    y = torch.empty((B, lin.d_out), dtype=torch.float32, device=dev)
+                    need = aqd.aqd_gemm_small_batch_workspace_bytes(lin.d_out, lin.d_in, lin.M, B)
+                    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=dev)
+
+                    def run(c):
+                        aqd.aqd_gemm_small_batch(cps[c], cbd, sd, k, xb, lin.d_out, lin.d_in, lin.M, dts[mode],
+                                                 out=y, workspace=ws)
+                    for c in range(copies):
+                        run(c)
+                    torch.cuda.synchronize()
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(reps):
+                        for c in range(copies):
+                            run(c)
+                    b.record()
+                    torch.cuda.synchronize()
+                    us = a.elapsed_time(b) * 1e3 / (reps * copies)
+                    xbytes = (4 if mode == "bf16x2" else 2) * B * lin.d_in
+                    byts = k * lin.d_out * (lin.d_in // 8) + xbytes + 4 * B * lin.d_out
+                    flops = 2.0 * B * lin.d_out * lin.d_in
+                    res.append({"shape": [lin.d_out, lin.d_in], "mode": mode, "k": k, "batch": B, "us": us,
+                                "tokens_per_s": B * 1e6 / us,
+                                "frac_hbm_peak": byts / us / 1e3 / HBM_PEAK_GBPS,
+                                "frac_mfma_peak": flops / us / 1e6 / 2500.0})
+        del cps, packed0
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -80,11 +220,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU work for the oracle baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline (profiling runs)")
-    ap.add_argument("--no-graph", action="store_true", help="skip the graph-captured sustained measurement")
+    ap.add_argument("--no-eager", action="store_true", help="skip the eager (one Python call per launch) timing")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decoder-stack measurement")
+    ap.add_argument("--no-small-batch", action="store_true", help="skip the small-batch matrix-core measurement")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one plain 64 MiB device copy first (scale reference for memory counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU sharding is not part of "
-                                   "this build (see the design notes on how the path would shard)"}))
+        print(json.dumps({"error": "bench.py measures one GPU only: the library has no multi-GPU path "
+                                   "(each GPU would run the same kernels on its own shard of rows)"}))
         sys.exit(2)
 
     import torch
@@ -109,86 +253,90 @@ def main():
     if need:
         ws = torch.zeros(need, dtype=torch.uint8, device=dev)
 
-    # quick sanity of the timed configuration against the oracle on sampled rows
-    import oracle
-    orc = oracle.load()
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     aqd.aqd_hadamard_rotate(xd, BLOCK, aqd.AQD_F16, out=xr)
-    rows = np.arange(0, D_OUT, 37)
-    worst = 0.0
-    for k in KS:
-        y = aqd.aqd_gemv(copies[5], cbd, sd, k, xr, D_OUT, D_IN, M, out=ys[k], workspace=ws)
-        ref = orc.forward(codes[rows], cb, s[rows], k, x, BLOCK)
-        got = y.cpu().numpy().astype(np.float64)[:, rows]
-        worst = max(worst, float(np.max(np.abs(got - ref)) / np.max(np.abs(ref))))
-    assert worst <= 2e-3, f"parity check failed before timing: {worst}"
+    y_check = {k: aqd.aqd_gemv(copies[5], cbd, sd, k, xr, D_OUT, D_IN, M, out=ys[k], workspace=ws).cpu().numpy()
+               for k in KS}
 
     stream = torch.cuda.current_stream()
     ctr = [0]
 
-    def step(events=None):
+    def gemv(k):
+        c = copies[ctr[0] % N_COPIES]
+        ctr[0] += 1
+        aqd.aqd_gemv(c, cbd, sd, k, xr, D_OUT, D_IN, M, out=ys[k], workspace=ws)
+
+    def rotate():
         aqd.aqd_hadamard_rotate(xd, BLOCK, aqd.AQD_F16, out=xr)
-        if events is not None:
-            events[0].record(stream)
-        for i, k in enumerate(KS):
-            c = copies[ctr[0] % N_COPIES]
-            ctr[0] += 1
-            aqd.aqd_gemv(c, cbd, sd, k, xr, D_OUT, D_IN, M, out=ys[k], workspace=ws)
-            if events is not None:
-                events[i + 1].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        rotate()
+        for k in KS:
+            gemv(k)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KS) + 1)] for _ in range(args.steps)]
+    # The K timed steps are issued kernel-major: K rotations, then K GEMVs at k = 1, then K at k = 2, ...
+    # Every step's work is done exactly once.  Each run of K launches of one kernel is captured in a
+    # graph (a Python launch costs more than a short kernel takes) and the graphs are replayed between
+    # events on the launch stream, so every event pair brackets K launches of one kernel.
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(args.steps):
+                    fn()
+        stream.wait_stream(side)
+        return g
+
+    graphs = [capture(rotate)] + [capture(lambda k=k: gemv(k)) for k in KS]
+    for g in graphs:
+        g.replay()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
+    evs[0].record(stream)
+    for i, g in enumerate(graphs):
+        g.replay()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    per_k_ms = {k: [] for k in KS}
-    for e in evs:
-        for i, k in enumerate(KS):
-            per_k_ms[k].append(e[i].elapsed_time(e[i + 1]))
+    gpu_ms = evs[0].elapsed_time(evs[-1])
+    rot_us = evs[0].elapsed_time(evs[1]) * 1e3 / args.steps
     per_k = {}
-    for k in KS:
-        us = float(np.mean(per_k_ms[k])) * 1e3
+    for i, k in enumerate(KS):
+        us = evs[i + 1].elapsed_time(evs[i + 2]) * 1e3 / args.steps
         per_k[k] = {
             "us_per_gemv": us,
-            "us_p10": float(np.percentile(per_k_ms[k], 10)) * 1e3,
-            "us_p90": float(np.percentile(per_k_ms[k], 90)) * 1e3,
             "code_bytes": code_bytes(k),
             "algorithmic_bytes": algorithmic_bytes(k),
             "GBps": algorithmic_bytes(k) / us / 1e3,
             "frac_hbm_peak": algorithmic_bytes(k) / us / 1e3 / HBM_PEAK_GBPS,
+            "frac_hbm_peak_code_stream": code_bytes(k) / us / 1e3 / HBM_PEAK_GBPS,
         }
+    del graphs
 
-    # sustained: 64 back-to-back GEMVs on distinct cold copies inside one captured graph
-    if not args.no_graph:
+    # the same launches issued one by one from Python (launch-rate bound for the short kernels)
+    if not args.no_eager:
+        reps = 50
         for k in KS:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(stream)
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(g, stream=side):
-                    for c in range(N_COPIES):
-                        aqd.aqd_gemv(copies[c], cbd, sd, k, xr, D_OUT, D_IN, M, out=ys[k], workspace=ws)
-            stream.wait_stream(side)
-            g.replay()
-            torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
             a.record(stream)
             for _ in range(reps):
-                g.replay()
+                gemv(k)
             b.record(stream)
             torch.cuda.synchronize()
-            us = a.elapsed_time(b) * 1e3 / (reps * N_COPIES)
-            per_k[k]["us_graph_sustained"] = us
-            per_k[k]["frac_hbm_peak_graph"] = algorithmic_bytes(k) / us / 1e3 / HBM_PEAK_GBPS
-            del g
+            per_k[k]["us_per_gemv_eager"] = a.elapsed_time(b) * 1e3 / reps
+
+    stack = None if args.no_stack else measure_stack(aqd, wl, torch, dev)
+    small = None if args.no_small_batch else measure_small_batch(aqd, wl, torch, dev)
 
     value = float(np.mean([per_k[k]["us_per_gemv"] for k in KS]))
     k4 = per_k[4]
@@ -199,7 +347,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall * 1e3 / args.steps,
+        "ms_per_step": gpu_ms / args.steps,
+        "ms_per_step_host_wall": wall * 1e3 / args.steps,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -210,8 +359,9 @@ def main():
                         "M=4 uint8 code planes, g=8, fp16 codebooks N(0,0.05), fp16 scales U(0.5,1.5), "
                         "Hadamard block 256, k=1..4, 64 cold copies of the codes",
             "d_out": D_OUT, "d_in": D_IN, "M": M, "k": list(KS), "batch": BATCH, "block": BLOCK,
-            "accumulate": "f32", "cold_copies": N_COPIES, "parity_sampled_rows_worst_err": worst,
+            "accumulate": "f32", "cold_copies": N_COPIES,
         },
+        "us_rotation": rot_us,
         "per_k": {str(k): v for k, v in per_k.items()},
         "roofline": {
             "bound": "hbm",
@@ -223,8 +373,12 @@ def main():
             "traffic": None,
         },
     }
+    if stack is not None:
+        result["stack"] = stack
+    if small is not None:
+        result["small_batch"] = small
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(codes, cb, s, x, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(codes, cb, s, x, args.cpu_budget, y_check)
     print(json.dumps(result))
 
 

@@ -52,7 +52,7 @@ typedef enum aqd_status {
     AQD_ERR_K = 3,           /* k outside [1, M] */
     AQD_ERR_BLOCK = 4,       /* Hadamard block not in {64,128,256} or does not divide d_in */
     AQD_ERR_DTYPE = 5,       /* unsupported dtype combination */
-    AQD_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+    AQD_ERR_ALIGN = 6,       /* a pointer is not aligned as the call requires */
     AQD_ERR_UNSUPPORTED = 7, /* group != 8 or code_bits != 8 */
     AQD_ERR_WORKSPACE = 8,   /* workspace missing or smaller than required */
     AQD_ERR_HIP = 9          /* a HIP runtime call failed; see aqd_last_error() */
@@ -159,18 +159,24 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
                     const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Small-batch product, batch 1..64: code tiles are dequantized (codeword sums
- * in fp32) into LDS as bf16 and multiplied on the bf16 matrix cores with fp32
- * accumulation.  The weight tile is kept as bf16 hi + lo (two MFMA terms),
- * and an AQD_BF16X2 activation adds its lo plane as a third term, so the
- * product keeps close to fp32 accuracy.
+ * Small-batch product, batch 1..64, on the matrix cores.  Each wave rebuilds
+ * the weight slice its MFMA operand holds from the codes (codeword sums) and
+ * multiplies it with 16-column tiles of the rotated activation, accumulating in
+ * fp32 (v_mfma_f32_16x16x32).
  *
  * y[n][i] = s_i * sum_j sum_{m<k} < C_m[codes[i][j][m]], x_rot[n][8j .. 8j+8) >   (fp32)
  *
- * x_rot:  AQD_BF16 [batch][d_in] or AQD_BF16X2 [2][batch][d_in] (x_dtype).
+ * x_dtype selects the operand precision:
+ *   AQD_BF16    x_rot bf16 [batch][d_in]; weights as bf16 hi + lo (2 bf16 passes)
+ *   AQD_BF16X2  x_rot [2][batch][d_in] bf16 hi, lo planes; 3 bf16 passes
+ *               (weights hi and lo against the activation hi, weights hi
+ *               against the activation lo): close to fp32 accuracy
+ *   AQD_F16     x_rot fp16 [batch][d_in]; weights as fp16 codeword sums; one
+ *               fp16 pass (same MFMA rate as bf16, 2^-11 operand rounding)
  * y:      fp32 [batch][d_out], overwritten.
- * Other arguments as for aqd_gemv; workspace follows the same zero-filled
- * contract with aqd_gemm_small_batch_workspace_bytes(layer, batch) bytes.
+ * workspace: aqd_gemm_small_batch_workspace_bytes(layer, batch) bytes (split
+ *         partials, fully overwritten by every call; NULL when 0).  Other
+ *         arguments as for aqd_gemv.  Results are bit-reproducible.
  * ------------------------------------------------------------------------- */
 size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch);
 

@@ -107,16 +107,20 @@ def test_empty_layer_is_a_no_op(L):
 
 
 def test_small_batch_rejects_bad_arguments(L):
-    def sb(k=1, batch=16, x_dt=BF16X2, layer=None, y=FAKE, x=FAKE):
+    def sb(k=1, batch=16, x_dt=BF16X2, layer=None, y=FAKE, x=FAKE, ws=FAKE, ws_bytes=1 << 30):
         return L.aqd_gemm_small_batch(FAKE, FAKE, FAKE, k, x, x_dt, y, batch, layer if layer is not None else lay(),
-                                      None, 0, None)
+                                      ws, ws_bytes, None)
     assert sb(batch=0) == E_SHAPE
     assert sb(batch=65) == E_SHAPE
     assert sb(k=0) == E_K
-    assert sb(x_dt=F16) == E_DTYPE
     assert sb(x_dt=F32) == E_DTYPE
-    assert sb(y=FAKE + 4) == E_ALIGN
+    assert sb(y=FAKE + 2) == E_ALIGN
     assert sb(x=None) == E_NULL
+    big = lay(4096, 14336, 4)
+    need = L.aqd_gemm_small_batch_workspace_bytes(big, 16)
+    assert need > 0                                   # the input dimension is split over workgroups
+    assert sb(layer=big, ws=None, ws_bytes=0) == E_WS
+    assert sb(layer=big, ws_bytes=need - 1) == E_WS
 
 
 def test_hadamard_rejects_bad_arguments(L):

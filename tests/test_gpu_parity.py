@@ -230,14 +230,22 @@ def test_small_batch_config(orc, name):
     packed = aqd.aqd_pack_codes(cdev)
     xd = to_dev(x, bf16_bits=True)
     xr = aqd.aqd_hadamard_rotate(xd, lin.block, aqd.AQD_BF16X2)
+    xr16 = aqd.aqd_hadamard_rotate(xd, lin.block, aqd.AQD_F16)
     for k in lin.ks:
         ref = orc.forward(codes, cb, s, k, x, lin.block, "bf16")
         for B in lin.batches:
             xb = xr[:, :B].contiguous()
             y = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xb, lin.d_out, lin.d_in, 4, aqd.AQD_BF16X2)
             e = normwise(y.cpu().numpy(), ref[:B])
-            record(test="small_batch", layer=name, k=k, batch=B, err=e, rms=rms_rel(y.cpu().numpy(), ref[:B]))
+            record(test="small_batch", mode="bf16x2", layer=name, k=k, batch=B, err=e,
+                   rms=rms_rel(y.cpu().numpy(), ref[:B]))
             assert e <= TOL, (k, B, e)
+            yf = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xr16[:B].contiguous(), lin.d_out, lin.d_in, 4,
+                                          aqd.AQD_F16)
+            ef = normwise(yf.cpu().numpy(), ref[:B])
+            record(test="small_batch", mode="f16", layer=name, k=k, batch=B, err=ef,
+                   rms=rms_rel(yf.cpu().numpy(), ref[:B]))
+            assert ef <= TOL, (k, B, ef)
 
 
 @pytest.mark.parametrize("d_out,d_in,M,batches", [(1000, 1000, 3, (1, 17, 64)), (16, 64, 1, (16,))])
@@ -260,6 +268,10 @@ def test_small_batch_edge_shapes(orc, d_out, d_in, M, batches):
             e = normwise(y, ref[:B])
             record(test="small_batch_edge", shape=[d_out, d_in, M], k=k, batch=B, err=e)
             assert e <= TOL, (k, B, e)
+            y1 = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, hi[:B].contiguous(), d_out, d_in, M,
+                                          aqd.AQD_BF16).cpu().numpy()
+            r1 = orc.linear(codes, cb, s, k, hi[:B].double().cpu().numpy())
+            assert normwise(y1, r1) <= TOL, (k, B)
 
 
 def test_small_batch_dyadic_bit_exact(orc):
@@ -268,10 +280,13 @@ def test_small_batch_dyadic_bit_exact(orc):
     cdev, cbdev, sdev = _layer_dev(codes, cb, s)
     packed = aqd.aqd_pack_codes(cdev)
     xb = torch.from_numpy(x.astype(np.float32)).to(dev()).to(torch.bfloat16).contiguous()
+    xh = torch.from_numpy(x).to(dev()).contiguous()
     for k in (1, 2):
         ref = orc.linear(codes, cb, s, k, x)
         y = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xb, d_out, d_in, M, aqd.AQD_BF16).cpu().numpy()
         assert np.array_equal(y.astype(np.float64), ref), k
+        yh = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xh, d_out, d_in, M, aqd.AQD_F16).cpu().numpy()
+        assert np.array_equal(yh.astype(np.float64), ref), k
 
 
 def test_quantized_linear_forward(orc):
@@ -303,3 +318,55 @@ def test_gemv_workspace_reusable_and_deterministic(orc):
     assert torch.equal(outs[0], outs[2])       # same inputs, same bits
     ref = orc.forward(codes, cb, s, 2, x, lin.block)
     assert normwise(outs[3].cpu().numpy(), ref) <= TOL
+
+
+def test_graph_replay_matches_eager(orc):
+    """Rotation, batch-1 GEMV and small-batch product captured in one HIP graph: every replay, with eager
+    work on the same workspaces in between, gives the eager result bit for bit."""
+    lin = wl.config(2)[0]
+    codes, cb, s, x = wl.layer_inputs(2, lin)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xd = to_dev(x)
+    xs = to_dev(wl.gen_x(wl.rng(81), 32, lin.d_in, "f16"))
+    ws1 = torch.zeros(max(aqd.aqd_gemv_workspace_bytes(lin.d_out, lin.d_in, lin.M, 1), 16), dtype=torch.uint8,
+                      device=dev())
+    ws2 = torch.zeros(max(aqd.aqd_gemm_small_batch_workspace_bytes(lin.d_out, lin.d_in, lin.M, 32), 16),
+                      dtype=torch.uint8, device=dev())
+    xr = torch.empty_like(xd)
+    xsr = torch.empty_like(xs)
+    y1 = torch.empty((1, lin.d_out), dtype=torch.float16, device=dev())
+    y2 = torch.empty((32, lin.d_out), dtype=torch.float32, device=dev())
+
+    def work():
+        aqd.aqd_hadamard_rotate(xd, lin.block, aqd.AQD_F16, out=xr)
+        aqd.aqd_gemv(packed, cbdev, sdev, 3, xr, lin.d_out, lin.d_in, lin.M, out=y1, workspace=ws1)
+        aqd.aqd_hadamard_rotate(xs, lin.block, aqd.AQD_F16, out=xsr)
+        aqd.aqd_gemm_small_batch(packed, cbdev, sdev, 2, xsr, lin.d_out, lin.d_in, lin.M, aqd.AQD_F16, out=y2,
+                                 workspace=ws2)
+
+    work()
+    torch.cuda.synchronize()
+    e1, e2 = y1.clone(), y2.clone()
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            work()
+    stream.wait_stream(side)
+    for rep in range(3):
+        y1.zero_()
+        y2.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y1, e1), rep
+        assert torch.equal(y2, e2), rep
+        # eager calls on the same workspaces between replays
+        aqd.aqd_gemv(packed, cbdev, sdev, 1, xr, lin.d_out, lin.d_in, lin.M, workspace=ws1)
+        aqd.aqd_gemm_small_batch(packed, cbdev, sdev, 4, xsr, lin.d_out, lin.d_in, lin.M, aqd.AQD_F16,
+                                 workspace=ws2)
+        torch.cuda.synchronize()
+    ref = orc.forward(codes, cb, s, 3, x, lin.block)
+    assert normwise(e1.float().cpu().numpy(), ref) <= TOL
