@@ -38,6 +38,19 @@ KS = (1, 2, 3, 4)
 N_COPIES = 64
 CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 and 4096 x 14336)
 
+# HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
+# only for the kernel source they were taken on: the summary under profiles/ gives the commands.
+TRAFFIC_K4_BYTES = 30662381
+TRAFFIC_K4_SOURCE_SHA256_PREFIX = "149ccb187f56ffdc"
+
+
+def measured_traffic():
+    import hashlib
+    src = os.path.join(ROOT, "additive_codebook_gemv_amd", "csrc", "gemv_lut.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return TRAFFIC_K4_BYTES if digest.startswith(TRAFFIC_K4_SOURCE_SHA256_PREFIX) else None
+
 
 def algorithmic_bytes(k: int, d_out: int = D_OUT, d_in: int = D_IN, batch: int = BATCH) -> int:
     """Bytes the k-codebook GEMV must move: codes, codebooks, scales, activation in, output out."""
@@ -370,7 +383,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": k4["frac_hbm_peak"],
-            "traffic": None,
+            "traffic": measured_traffic(),
         },
     }
     if stack is not None:
