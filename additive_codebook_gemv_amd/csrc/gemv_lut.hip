@@ -59,9 +59,18 @@ struct LutArgs {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Streaming 16-byte load of codes that are read exactly once.
-__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
-    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+// Buffer descriptor over the row tiles of one slot (the dword-3 format word of
+// the gfx9 family for raw byte-addressed buffers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const uint8_t* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Streaming 16-byte load of codes that are read exactly once (nontemporal).
+// An offset past the end of the descriptor returns zeros without touching
+// memory, which is how a wave without a tile keeps its load count fixed.
+constexpr uint32_t NO_TILE = 0x80000000u;
+__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -151,14 +160,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     // Every load below is unconditional (inactive slots, padding groups and
     // missing tiles read a valid address and the value is replaced by zero), so
     // the compiler can wait for exactly the loads a step needs.
-    int64_t slot_off[LUT_SLOTS];
+    __amdgpu_buffer_rsrc_t slot_buf[LUT_SLOTS];
     bool slot_on[LUT_SLOTS];
 #pragma unroll
     for (int s = 0; s < LUT_SLOTS; ++s) {
         const int q = slice * LUT_SLOTS + s;
         slot_on[s] = q < p.n_slots;
         const int qq = slot_on[s] ? q : 0;
-        slot_off[s] = (int64_t)(qq % K) * p.plane_bytes + (int64_t)(qq / K) * p.n_rt * TILE_BYTES + lane * TILE_ROWS;
+        slot_buf[s] = slot_rsrc(p.packed + (int64_t)(qq % K) * p.plane_bytes + (int64_t)(qq / K) * p.n_rt * TILE_BYTES,
+                                p.n_rt * TILE_BYTES);
     }
 
     // ---- table operands first (loads complete in order)
@@ -183,15 +193,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         }
     }
 
-    // ---- then every code tile of this wave (at most LUT_TILES_PER_WAVE), so the
-    // wave's whole share of the code stream is in flight while the tables are built
+    // Vector memory requests of a CU are served in issue order, so a wave's table
+    // operands would otherwise queue behind the code tiles other waves issued
+    // earlier and the build could only start once the whole stream had arrived.
+    // Every wave issues its operand loads before any wave issues a code load.
+    __builtin_amdgcn_s_barrier();
+
+    // ---- then the first code tile of every wave: half of the workgroup's code
+    // stream is in flight while the tables are built.  The second half is
+    // requested only after the build (below): requests issued earlier would sit
+    // in front of other workgroups' table operands and delay every build.
     uint4 codes[LUT_TILES_PER_WAVE][LUT_SLOTS];
+    auto load_tile = [&](int u) {
+        const int64_t it = t0 + wave + (int64_t)u * WAVES;
+        const uint32_t off = it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE;
+#pragma unroll
+        for (int s = 0; s < LUT_SLOTS; ++s) codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
+    };
+    load_tile(0);
+    // scales of the rows this lane may finish (needed only at the end; clamped)
+    uint16_t row_scale[LUT_TILES_PER_WAVE];
 #pragma unroll
     for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
-        const int64_t it = t0 + wave + (int64_t)u * WAVES;
-        const int64_t itc = it < t1 ? it : t0;
-#pragma unroll
-        for (int s = 0; s < LUT_SLOTS; ++s) codes[u][s] = load_stream(p.packed + slot_off[s] + itc * TILE_BYTES);
+        const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
+        row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
@@ -221,6 +246,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         }
     }
     __syncthreads();
+#pragma unroll
+    for (int u = 1; u < LUT_TILES_PER_WAVE; ++u) load_tile(u);
 
     uint32_t base[LUT_SLOTS];
 #pragma unroll
@@ -275,7 +302,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         if (row >= p.d_out) continue;
         const unsigned long long biased = (old_word[u] & ((1ull << FIX_COUNT_SHIFT) - 1)) + term[u];
         const long long total = (long long)biased - (long long)p.slices * (long long)FIX_BIAS;
-        p.y[row] = f2h(h2f(p.scales[row]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
+        p.y[row] = f2h(h2f(row_scale[u]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
         __hip_atomic_store(p.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
