@@ -178,6 +178,45 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
     }
 
 
+def measure_batched_gemv(aqd, torch, dev, copies, cbd, sd, stream, reps: int = 3):
+    """The GEMV at batch 2, 4 and 8 on the timed layer (the code stream is read once for all columns),
+    k = 1..4, each over a captured graph of back-to-back launches on the cold copies."""
+    res = []
+    g = np.random.Generator(np.random.PCG64(0xB2))
+    for B in (2, 4, 8):
+        xr = torch.from_numpy(g.standard_normal((B, D_IN)).astype(np.float16)).to(dev)
+        y = torch.empty((B, D_OUT), dtype=torch.float16, device=dev)
+        need = aqd.aqd_gemv_workspace_bytes(D_OUT, D_IN, M, B)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=dev)
+        for k in KS:
+            def run():
+                for c in copies:
+                    aqd.aqd_gemv(c, cbd, sd, k, xr, D_OUT, D_IN, M, out=y, workspace=ws)
+            run()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    run()
+            stream.wait_stream(side)
+            graph.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / (reps * len(copies))
+            byts = algorithmic_bytes(k, batch=B)
+            res.append({"batch": B, "k": k, "us": us, "tokens_per_s": B * 1e6 / us,
+                        "frac_hbm_peak": byts / us / 1e3 / HBM_PEAK_GBPS})
+            del graph
+    return res
+
+
 def measure_small_batch(aqd, wl, torch, dev, copies: int = 32, reps: int = 2):
     """The matrix-core path on the 14336x4096 and 4096x14336 shapes at batch 16/32/64, k = 4 and 2, with
     the activation as bf16 hi/lo planes (three bf16 passes) and as fp16 (one pass)."""
@@ -236,6 +275,7 @@ def main():
     ap.add_argument("--no-eager", action="store_true", help="skip the eager (one Python call per launch) timing")
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decoder-stack measurement")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the small-batch matrix-core measurement")
+    ap.add_argument("--no-batched", action="store_true", help="skip the batch 2/4/8 GEMV measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 64 MiB device copy first (scale reference for memory counters)")
     args = ap.parse_args()
@@ -348,6 +388,7 @@ def main():
             torch.cuda.synchronize()
             per_k[k]["us_per_gemv_eager"] = a.elapsed_time(b) * 1e3 / reps
 
+    batched = None if args.no_batched else measure_batched_gemv(aqd, torch, dev, copies, cbd, sd, stream)
     stack = None if args.no_stack else measure_stack(aqd, wl, torch, dev)
     small = None if args.no_small_batch else measure_small_batch(aqd, wl, torch, dev)
 
@@ -386,6 +427,8 @@ def main():
             "traffic": measured_traffic(),
         },
     }
+    if batched is not None:
+        result["gemv_batch_2_4_8"] = batched
     if stack is not None:
         result["stack"] = stack
     if small is not None:
