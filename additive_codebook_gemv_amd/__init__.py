@@ -35,6 +35,13 @@ class aqd_layer(ctypes.Structure):
                 ("group", ctypes.c_int32), ("code_bits", ctypes.c_int32)]
 
 
+class aqd_linear(ctypes.Structure):
+    _fields_ = [("packed_codes", ctypes.c_void_p), ("codebooks", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("M", ctypes.c_int32)]
+
+
+AQD_MAX_GROUP = 4
+
 _lib: Optional[ctypes.CDLL] = None
 
 _VP, _SZ, _I32, _I64, _INT = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64, ctypes.c_int
@@ -49,6 +56,8 @@ _SIGNATURES = {
     "aqd_hadamard_rotate": (_INT, [_VP, _VP, _INT, _INT, _I64, _I64, _I32, _VP]),
     "aqd_gemv_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemv": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
+    "aqd_gemv_grouped_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_linear), _I32, _I64]),
+    "aqd_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
 }
@@ -151,6 +160,42 @@ def aqd_gemv(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor
                           ctypes.byref(L), _ptr(workspace), workspace.numel() if workspace is not None else 0,
                           _stream()))
     return out
+
+
+def _linears(parts):
+    arr = (aqd_linear * len(parts))()
+    for i, (packed, codebooks, scales, y, d_out, M) in enumerate(parts):
+        arr[i] = aqd_linear(_ptr(packed), _ptr(codebooks), _ptr(scales), _ptr(y), d_out, M)
+    return arr
+
+
+def aqd_gemv_grouped_workspace_bytes(d_outs, d_in: int, Ms) -> int:
+    arr = (aqd_linear * len(d_outs))()
+    for i, (d_out, M) in enumerate(zip(d_outs, Ms)):
+        arr[i] = aqd_linear(None, None, None, None, d_out, M)
+    return int(lib().aqd_gemv_grouped_workspace_bytes(arr, len(d_outs), d_in))
+
+
+def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
+                     workspace: Optional[torch.Tensor] = None):
+    """Batch-1 GEMV of several linears sharing x_rot (fp16 [d_in] or [1][d_in]) in one launch.
+
+    linears: sequence of (packed, codebooks, scales, d_out, M) or (packed, codebooks, scales, d_out, M, out);
+    returns the fp16 outputs [1][d_out], one per linear.
+    """
+    outs, parts = [], []
+    for lin in linears:
+        packed, codebooks, scales, d_out, M = lin[:5]
+        y = lin[5] if len(lin) > 5 else torch.empty((1, d_out), dtype=torch.float16, device=x_rot.device)
+        outs.append(y)
+        parts.append((packed, codebooks, scales, y, d_out, M))
+    arr = _linears(parts)
+    need = int(lib().aqd_gemv_grouped_workspace_bytes(arr, len(parts), d_in))
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
+    _check(lib().aqd_gemv_grouped(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0, _stream()))
+    return outs
 
 
 def aqd_gemm_small_batch_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:

@@ -58,6 +58,18 @@ size_t gemv_lut_workspace_bytes(const Geometry& g);
 bool gemv_lut_supported(const Geometry& g, int batch, int k);
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                            const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s);
+// several batch-1 linears sharing one input and k, in one launch
+struct LutLinearRef {
+    const uint8_t* packed;
+    const uint16_t* codebooks;
+    const uint16_t* scales;
+    uint16_t* y;
+    int64_t d_out;
+};
+bool gemv_lut_grouped_supported(int64_t G, int k);
+size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n);
+hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
+                                   void* ws, hipStream_t s);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,

@@ -149,6 +149,59 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
                       "aqd_gemv");
 }
 
+static aqd_status check_group(const aqd_linear* lins, int32_t n, int64_t d_in, aqd_layer* layers) {
+    if (!lins) return fail(AQD_ERR_NULL, "linears is NULL");
+    if (n < 1 || n > AQD_MAX_GROUP) return fail(AQD_ERR_SHAPE, "n_linears must be in [1, AQD_MAX_GROUP]");
+    for (int i = 0; i < n; ++i) {
+        layers[i] = aqd_layer{lins[i].d_out, d_in, lins[i].M, 8, 8};
+        aqd_status st = check_layer(&layers[i]);
+        if (st != AQD_OK) return st;
+    }
+    return AQD_OK;
+}
+
+size_t aqd_gemv_grouped_workspace_bytes(const aqd_linear* linears, int32_t n_linears, int64_t d_in) {
+    aqd_layer layers[AQD_MAX_GROUP];
+    if (check_group(linears, n_linears, d_in, layers) != AQD_OK) return 0;
+    int64_t d_out[AQD_MAX_GROUP];
+    for (int i = 0; i < n_linears; ++i) d_out[i] = linears[i].d_out;
+    return gemv_lut_grouped_workspace_bytes(d_out, n_linears);
+}
+
+aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
+                            int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+    aqd_layer layers[AQD_MAX_GROUP];
+    aqd_status st = check_group(linears, n_linears, d_in, layers);
+    if (st != AQD_OK) return st;
+    const size_t need = aqd_gemv_grouped_workspace_bytes(linears, n_linears, d_in);
+    bool any = false;
+    for (int i = 0; i < n_linears; ++i) {
+        bool nothing = false;
+        st = check_product(linears[i].packed_codes, linears[i].codebooks, linears[i].scales, k, x_rot,
+                           linears[i].y, &layers[i], workspace, workspace_bytes, need, &nothing);
+        if (st != AQD_OK) return st;
+        any = any || !nothing;
+    }
+    if (!any) return AQD_OK;
+    if (d_in == 0) {        // empty input: every y is zero (no tables to build)
+        for (int i = 0; i < n_linears; ++i) {
+            if (linears[i].d_out == 0) continue;
+            st = aqd_gemv(linears[i].packed_codes, linears[i].codebooks, linears[i].scales, k, x_rot,
+                          linears[i].y, 1, &layers[i], workspace, workspace_bytes, stream);
+            if (st != AQD_OK) return st;
+        }
+        return AQD_OK;
+    }
+    if (!gemv_lut_grouped_supported(d_in / 8, k))
+        return fail(AQD_ERR_UNSUPPORTED, "input too wide for one grouped launch");
+    LutLinearRef refs[AQD_MAX_GROUP];
+    for (int i = 0; i < n_linears; ++i)
+        refs[i] = LutLinearRef{linears[i].packed_codes, linears[i].codebooks, linears[i].scales, linears[i].y,
+                               linears[i].d_out};
+    return hip_status(launch_gemv_lut_grouped(refs, n_linears, k, x_rot, d_in, workspace, (hipStream_t)stream),
+                      "aqd_gemv_grouped");
+}
+
 size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch) {
     if (check_layer(layer) != AQD_OK || batch < 1 || batch > 64) return 0;
     return gemm_sb_workspace_bytes(geometry(*layer), batch);

@@ -45,16 +45,26 @@ constexpr int LUT_BYTES = (LUT_SLOTS / 2) * LUT_PAIR_BYTES;  // 128 KiB
 constexpr int LUT_CUS = 256;                                  // one 128 KiB workgroup per CU
 constexpr int LUT_WAVES = 16;
 constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles a wave keeps in flight
+constexpr int LUT_MAX_GROUP = AQD_MAX_GROUP;                  // linears per launch
 
-struct LutArgs {
+// One linear of a launch.  Several linears that share the input (and k) run
+// in one launch: their workgroups follow each other in the grid.
+struct LutLinear {
     const uint8_t* packed;
     const uint16_t* codebooks;
     const uint16_t* scales;
-    const uint16_t* x;
     uint16_t* y;
     unsigned long long* acc;  // workspace: [d_out] counted fixed-point row sums, zero between calls
-    int64_t d_out, G, n_rt, n_gt, plane_bytes;
-    int k, n_slots, slices, tiles_per_block;
+    int64_t d_out, n_rt, plane_bytes;
+    int tiles_per_block;
+    int wg_begin;             // first workgroup of this linear
+};
+
+struct LutArgs {
+    LutLinear lin[LUT_MAX_GROUP];
+    const uint16_t* x;
+    int64_t G, n_gt;
+    int k, n_slots, slices, n_lin;
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -145,16 +155,26 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
     return d;
 }
 
-template <int WAVES, int K>
+template <int WAVES, int K, bool MULTI>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     __shared__ __align__(16) uint8_t lds[LUT_BYTES + 16];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int slice = blockIdx.x % p.slices;
-    const int rb = blockIdx.x / p.slices;
-    const int64_t t0 = (int64_t)rb * p.tiles_per_block;
-    const int64_t t1 = t0 + p.tiles_per_block < p.n_rt ? t0 + p.tiles_per_block : p.n_rt;
+    // this workgroup's linear (uniform); a single-linear launch reads its fields
+    // at fixed offsets, without a second dependent argument load
+    int l = 0;
+    if (MULTI) {
+#pragma unroll
+        for (int i = 1; i < LUT_MAX_GROUP; ++i)
+            if (i < p.n_lin && (int)blockIdx.x >= p.lin[i].wg_begin) l = i;
+    }
+    const LutLinear L = p.lin[MULTI ? l : 0];
+    const int local = (int)blockIdx.x - L.wg_begin;
+    const int slice = local % p.slices;
+    const int rb = local / p.slices;
+    const int64_t t0 = (int64_t)rb * L.tiles_per_block;
+    const int64_t t1 = t0 + L.tiles_per_block < L.n_rt ? t0 + L.tiles_per_block : L.n_rt;
 
     // slot s of this slice: q = slice*4 + s -> group tile q / K, codebook q % K.
     // Every load below is unconditional (inactive slots, padding groups and
@@ -167,8 +187,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         const int q = slice * LUT_SLOTS + s;
         slot_on[s] = q < p.n_slots;
         const int qq = slot_on[s] ? q : 0;
-        slot_buf[s] = slot_rsrc(p.packed + (int64_t)(qq % K) * p.plane_bytes + (int64_t)(qq / K) * p.n_rt * TILE_BYTES,
-                                p.n_rt * TILE_BYTES);
+        slot_buf[s] = slot_rsrc(L.packed + (int64_t)(qq % K) * L.plane_bytes + (int64_t)(qq / K) * L.n_rt * TILE_BYTES,
+                                L.n_rt * TILE_BYTES);
     }
 
     // ---- table operands first (loads complete in order)
@@ -188,7 +208,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
             const int64_t g = (int64_t)(qq / K) * TILE_GROUPS + gb * 32 + (lane & 31);
             bok[u][h] = q < p.n_slots && g < p.G;
             const int64_t gc = g < p.G ? g : p.G - 1;
-            av[u][h] = *reinterpret_cast<const uint2*>(p.codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
+            av[u][h] = *reinterpret_cast<const uint2*>(L.codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
             bv[u][h] = *reinterpret_cast<const uint2*>(p.x + gc * GROUP + e0);
         }
     }
@@ -216,7 +236,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 #pragma unroll
     for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
-        row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
+        row_scale[u] = L.scales[row < L.d_out ? row : L.d_out - 1];
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
@@ -288,10 +308,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         }
         const float sum = fold_rows(rows, lane);
         const int64_t row = it * TILE_ROWS + (lane >> 2);
-        if ((lane & 3) == 0 && row < p.d_out) {
+        if ((lane & 3) == 0 && row < L.d_out) {
             mine[u] = true;
             term[u] = fix_term(sum);
-            old_word[u] = atomicAdd(p.acc + row, (1ull << FIX_COUNT_SHIFT) + term[u]);
+            old_word[u] = atomicAdd(L.acc + row, (1ull << FIX_COUNT_SHIFT) + term[u]);
         }
     }
 #pragma unroll
@@ -299,75 +319,116 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         if (!mine[u] || (int)(old_word[u] >> FIX_COUNT_SHIFT) != p.slices - 1) continue;
         // this lane added the last contribution of its row: it holds the complete sum
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
-        if (row >= p.d_out) continue;
+        if (row >= L.d_out) continue;
         const unsigned long long biased = (old_word[u] & ((1ull << FIX_COUNT_SHIFT) - 1)) + term[u];
         const long long total = (long long)biased - (long long)p.slices * (long long)FIX_BIAS;
-        p.y[row] = f2h(h2f(row_scale[u]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
-        __hip_atomic_store(p.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        L.y[row] = f2h(h2f(row_scale[u]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
+        __hip_atomic_store(L.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 // ---- host side ---------------------------------------------------------------
 
-struct LutPlan {
-    int slices, tiles_per_block, row_blocks;
-};
+static int lut_slices(int64_t n_gt, int k) { return (int)(((int64_t)k * n_gt + LUT_SLOTS - 1) / LUT_SLOTS); }
 
-static LutPlan lut_plan(const Geometry& g, int k) {
-    LutPlan pl;
-    const int64_t n_slots = (int64_t)k * g.n_gt;
-    pl.slices = (int)((n_slots + LUT_SLOTS - 1) / LUT_SLOTS);
-    int64_t rb = LUT_CUS / pl.slices;
-    if (rb < 1) rb = 1;
-    if (rb > g.n_rt) rb = g.n_rt;
-    int64_t tpb = (g.n_rt + rb - 1) / rb;
-    if (tpb > LUT_WAVES * LUT_TILES_PER_WAVE) tpb = LUT_WAVES * LUT_TILES_PER_WAVE;
-    pl.tiles_per_block = (int)tpb;
-    pl.row_blocks = (int)((g.n_rt + tpb - 1) / tpb);
-    return pl;
+// Row tiles per workgroup for each linear: the grid aims at one workgroup per
+// CU, shared among the linears in proportion to their rows; a workgroup holds
+// at most LUT_WAVES * LUT_TILES_PER_WAVE tiles.
+static void lut_plan(const int64_t* n_rt, int n, int slices, int* tpb, int* blocks) {
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) total += n_rt[i];
+    for (int i = 0; i < n; ++i) {
+        int64_t rb = total > 0 ? (LUT_CUS / slices) * n_rt[i] / total : 1;
+        if (rb < 1) rb = 1;
+        if (rb > n_rt[i]) rb = n_rt[i];
+        int64_t t = (n_rt[i] + rb - 1) / rb;
+        if (t > LUT_WAVES * LUT_TILES_PER_WAVE) t = LUT_WAVES * LUT_TILES_PER_WAVE;
+        tpb[i] = (int)t;
+        blocks[i] = (int)((n_rt[i] + t - 1) / t);
+    }
 }
 
-static size_t acc_bytes(const Geometry& g) { return ((size_t)g.d_out * 8 + 255) / 256 * 256; }
+static size_t acc_bytes(int64_t d_out) { return ((size_t)d_out * 8 + 255) / 256 * 256; }
 
-size_t gemv_lut_workspace_bytes(const Geometry& g) { return acc_bytes(g); }
+size_t gemv_lut_workspace_bytes(const Geometry& g) { return acc_bytes(g.d_out); }
 
 bool gemv_lut_supported(const Geometry& g, int batch, int k) {
-    const int64_t slices = ((int64_t)k * g.n_gt + LUT_SLOTS - 1) / LUT_SLOTS;
-    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && slices <= LUT_MAX_SLICES;
+    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && lut_slices(g.n_gt, k) <= LUT_MAX_SLICES;
+}
+
+bool gemv_lut_grouped_supported(int64_t G, int k) {
+    const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
+    return n_gt > 0 && lut_slices(n_gt, k) <= LUT_MAX_SLICES;
+}
+
+size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
+    size_t b = 0;
+    for (int i = 0; i < n; ++i) b += acc_bytes(d_out[i]);
+    return b;
+}
+
+template <bool MULTI>
+static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
+    switch (k) {
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI>), gd, bd, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI>), gd, bd, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI>), gd, bd, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI>), gd, bd, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI>), gd, bd, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI>), gd, bd, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI>), gd, bd, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI>), gd, bd, 0, s, a); break;
+    }
+}
+
+hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
+                                   void* ws, hipStream_t s) {
+    const int64_t G = d_in / GROUP;
+    const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
+    LutArgs a = {};
+    a.x = x;
+    a.G = G;
+    a.n_gt = n_gt;
+    a.k = k;
+    a.n_slots = (int)((int64_t)k * n_gt);
+    a.slices = lut_slices(n_gt, k);
+    int64_t n_rt[LUT_MAX_GROUP];
+    int tpb[LUT_MAX_GROUP], blocks[LUT_MAX_GROUP];
+    int m = 0;                                 // linears with rows
+    for (int i = 0; i < n; ++i)
+        if (lins[i].d_out > 0) {
+            a.lin[m].packed = lins[i].packed;
+            a.lin[m].codebooks = lins[i].codebooks;
+            a.lin[m].scales = lins[i].scales;
+            a.lin[m].y = lins[i].y;
+            a.lin[m].d_out = lins[i].d_out;
+            a.lin[m].n_rt = (lins[i].d_out + TILE_ROWS - 1) / TILE_ROWS;
+            a.lin[m].plane_bytes = a.lin[m].n_rt * n_gt * TILE_BYTES;
+            n_rt[m] = a.lin[m].n_rt;
+            ++m;
+        }
+    if (m == 0) return hipSuccess;
+    a.n_lin = m;
+    lut_plan(n_rt, m, a.slices, tpb, blocks);
+    uint8_t* acc = static_cast<uint8_t*>(ws);
+    int wg = 0;
+    for (int i = 0; i < m; ++i) {
+        a.lin[i].tiles_per_block = tpb[i];
+        a.lin[i].wg_begin = wg;
+        a.lin[i].acc = reinterpret_cast<unsigned long long*>(acc);
+        acc += acc_bytes(a.lin[i].d_out);
+        wg += a.slices * blocks[i];
+    }
+    const dim3 gd((unsigned)wg), bd(64 * LUT_WAVES);
+    if (m == 1) launch_k<false>(k, gd, bd, s, a);
+    else launch_k<true>(k, gd, bd, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                            const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s) {
-    const LutPlan pl = lut_plan(g, k);
-    LutArgs a;
-    a.packed = packed;
-    a.codebooks = codebooks;
-    a.scales = scales;
-    a.x = x;
-    a.y = y;
-    a.acc = static_cast<unsigned long long*>(ws);
-    a.d_out = g.d_out;
-    a.G = g.G;
-    a.n_rt = g.n_rt;
-    a.n_gt = g.n_gt;
-    a.plane_bytes = g.plane_bytes;
-    a.k = k;
-    a.n_slots = (int)((int64_t)k * g.n_gt);
-    a.slices = pl.slices;
-    a.tiles_per_block = pl.tiles_per_block;
-    const unsigned grid = (unsigned)(pl.slices * pl.row_blocks);
-    const dim3 gd(grid), bd(64 * LUT_WAVES);
-    switch (k) {
-        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1>), gd, bd, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2>), gd, bd, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3>), gd, bd, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4>), gd, bd, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5>), gd, bd, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6>), gd, bd, 0, s, a); break;
-        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7>), gd, bd, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8>), gd, bd, 0, s, a); break;
-    }
-    return hipGetLastError();
+    const LutLinearRef one = {packed, codebooks, scales, y, g.d_out};
+    return launch_gemv_lut_grouped(&one, 1, k, x, g.d_in, ws, s);
 }
 
 }  // namespace aqd

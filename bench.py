@@ -104,7 +104,9 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
     """One decode token through the synthetic 32-layer stack of 8B shape (linears and rotations only).
 
     Per layer: q/k/v share one rotated input, o, gate/up (shared) and down get their own; every linear
-    uses the layer's seeded k.  The 352 launches of a token are captured in one graph and replayed.
+    uses the layer's seeded k.  Two schedules of the same work, each captured in one graph and replayed:
+    grouped (q, k, v in one launch, gate and up in one launch: 4 rotations + 4 GEMV launches per layer)
+    and separate (4 rotations + 7 GEMV launches per layer).
     """
     lins = wl.config(4)
     ks = wl.stack_ks()
@@ -117,6 +119,8 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
         code_bytes += lin.ks[0] * lin.d_out * (lin.d_in // 8)
         del codes
     ws_need = max(aqd.aqd_gemv_workspace_bytes(l.d_out, l.d_in, l.M, 1) for l in lins)
+    ws_need = max(ws_need, aqd.aqd_gemv_grouped_workspace_bytes([4096, 1024, 1024], 4096, [4, 4, 4]),
+                  aqd.aqd_gemv_grouped_workspace_bytes([14336, 14336], 4096, [4, 4]))
     ws = torch.zeros(max(ws_need, 16), dtype=torch.uint8, device=dev)
     g = np.random.Generator(np.random.PCG64(0xA0D00004))
     inputs = {}
@@ -127,54 +131,79 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
     outs = [torch.empty((1, l.d_out), dtype=torch.float16, device=dev) for l in lins]
     src = {"q": "qkv", "k": "qkv", "v": "qkv", "o": "o", "gate": "mlp", "up": "mlp", "down": "down"}
 
-    def token():
+    def rotations(layer):
+        for name in ("qkv", "o", "mlp", "down"):
+            x, xr = inputs[(layer, name)]
+            aqd.aqd_hadamard_rotate(x, wl.block_for(x.shape[1]), aqd.AQD_F16, out=xr)
+
+    def token_separate():
         for layer in range(32):
-            for name in ("qkv", "o", "mlp", "down"):
-                x, xr = inputs[(layer, name)]
-                aqd.aqd_hadamard_rotate(x, wl.block_for(x.shape[1]), aqd.AQD_F16, out=xr)
+            rotations(layer)
             for j in range(7):
                 lin, packed, cb, sc = layers[layer * 7 + j]
                 xr = inputs[(layer, src[lin.proj])][1]
                 aqd.aqd_gemv(packed, cb, sc, lin.ks[0], xr, lin.d_out, lin.d_in, lin.M, out=outs[layer * 7 + j],
                              workspace=ws)
 
+    def token_grouped():
+        for layer in range(32):
+            rotations(layer)
+            for group in ((0, 1, 2), (3,), (4, 5), (6,)):
+                lin0 = layers[layer * 7 + group[0]][0]
+                xr = inputs[(layer, src[lin0.proj])][1]
+                if len(group) == 1:
+                    lin, packed, cb, sc = layers[layer * 7 + group[0]]
+                    aqd.aqd_gemv(packed, cb, sc, lin.ks[0], xr, lin.d_out, lin.d_in, lin.M,
+                                 out=outs[layer * 7 + group[0]], workspace=ws)
+                else:
+                    parts = [(p, c, s_, l.d_out, l.M, outs[layer * 7 + j])
+                             for j in group for (l, p, c, s_) in [layers[layer * 7 + j]]]
+                    aqd.aqd_gemv_grouped(parts, lin0.ks[0], xr, lin0.d_in, workspace=ws)
+
     stream = torch.cuda.current_stream()
-    token()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            token()
-    stream.wait_stream(side)
-    graph.replay()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(replays):
-        graph.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / replays
-    a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a2.record(stream)
-    for _ in range(3):
+
+    def timed(token):
         token()
-    b2.record(stream)
-    torch.cuda.synchronize()
-    us_eager = a2.elapsed_time(b2) * 1e3 / 3
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                token()
+        stream.wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(replays):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / replays
+        a2, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a2.record(stream)
+        for _ in range(3):
+            token()
+        b2.record(stream)
+        torch.cuda.synchronize()
+        return us, a2.elapsed_time(b2) * 1e3 / 3
+
+    us, us_eager = timed(token_grouped)
+    us_sep, us_sep_eager = timed(token_separate)
     return {
         "workload": "32-layer decoder stack of 8B shape (q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; "
-                    "down 4096x14336), batch 1, M=4, per-layer k from {2,3,4} (seeded), 4 rotations + 7 GEMVs "
-                    "per layer, linears and rotations only",
+                    "down 4096x14336), batch 1, M=4, per-layer k from {2,3,4} (seeded), linears and rotations "
+                    "only; q/k/v and gate/up grouped into one launch each",
         "layer_k": ks,
-        "launches_per_token": 32 * 11,
+        "launches_per_token": 32 * 8,
         "code_bytes_per_token": code_bytes,
         "us_per_token_graph": us,
         "tokens_per_s_graph": 1e6 / us,
         "us_per_token_eager": us_eager,
         "frac_hbm_peak_graph": code_bytes / us / 1e3 / HBM_PEAK_GBPS,
+        "separate_launches": {"launches_per_token": 32 * 11, "us_per_token_graph": us_sep,
+                              "us_per_token_eager": us_sep_eager},
     }
 
 

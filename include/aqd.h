@@ -159,6 +159,37 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
                     const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Grouped batch-1 GEMV: up to AQD_MAX_GROUP linears that read the same rotated
+ * input (q, k and v of an attention block; gate and up of an MLP) in one
+ * launch.  Each linear computes exactly what aqd_gemv computes for it at
+ * batch 1 (Drop-by-Drop, sections 3.2 and 5), with the same bits.
+ *
+ * linears:   n_linears descriptors (host memory, read during the call only):
+ *            packed codes, codebooks, scales and fp16 output y [d_out] of each
+ *            linear, as for aqd_gemv; group 8 and 8-bit codes.
+ * k:         codebooks used by every linear, 1..min M.
+ * x_rot:     fp16 [d_in], shared.
+ * workspace: aqd_gemv_grouped_workspace_bytes(linears, n_linears, d_in) bytes,
+ *            zero-filled before first use and left zeroed, as for aqd_gemv.
+ * Errors as for aqd_gemv; AQD_ERR_SHAPE for n_linears outside 1..AQD_MAX_GROUP.
+ * ------------------------------------------------------------------------- */
+#define AQD_MAX_GROUP 4
+
+typedef struct {
+    const uint8_t* packed_codes;
+    const uint16_t* codebooks;
+    const uint16_t* scales;
+    uint16_t* y;
+    int64_t d_out;
+    int32_t M;
+} aqd_linear;
+
+size_t aqd_gemv_grouped_workspace_bytes(const aqd_linear* linears, int32_t n_linears, int64_t d_in);
+
+aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
+                            int64_t d_in, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Small-batch product, batch 1..64, on the matrix cores.  Each wave rebuilds
  * the weight slice its MFMA operand holds from the codes (codeword sums) and
  * multiplies it with 16-column tiles of the rotated activation, accumulating in

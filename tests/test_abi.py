@@ -170,3 +170,23 @@ def test_gemv_workspace_required(L):
     assert _gemv(L, layer=lay(4096, 14336, 4), ws=None, ws_bytes=0) == E_WS
     assert _gemv(L, layer=lay(4096, 14336, 4), ws=FAKE, ws_bytes=need - 1) == E_WS
     assert _gemv(L, layer=lay(4096, 14336, 4), ws=FAKE_ODD, ws_bytes=need) == E_ALIGN
+
+
+def test_grouped_gemv_rejects_bad_arguments(L):
+    def lins(n, d_out=64, M=2):
+        arr = (aqd.aqd_linear * max(n, 1))()
+        for i in range(n):
+            arr[i] = aqd.aqd_linear(FAKE, FAKE, FAKE, FAKE, d_out, M)
+        return arr
+    big = lins(3, 4096, 4)
+    need = L.aqd_gemv_grouped_workspace_bytes(big, 3, 4096)
+    assert need >= 3 * 4096 * 8
+    assert L.aqd_gemv_grouped(lins(0), 0, 1, FAKE, 256, FAKE, 1 << 20, None) == E_SHAPE
+    assert L.aqd_gemv_grouped(lins(5), 5, 1, FAKE, 256, FAKE, 1 << 20, None) == E_SHAPE
+    assert L.aqd_gemv_grouped(None, 2, 1, FAKE, 256, FAKE, 1 << 20, None) == E_NULL
+    assert L.aqd_gemv_grouped(lins(2), 2, 3, FAKE, 256, FAKE, 1 << 20, None) == E_K          # M = 2
+    assert L.aqd_gemv_grouped(lins(2), 2, 1, FAKE, 100, FAKE, 1 << 20, None) == E_SHAPE      # d_in % 8
+    assert L.aqd_gemv_grouped(big, 3, 2, FAKE, 4096, None, 0, None) == E_WS
+    assert L.aqd_gemv_grouped(big, 3, 2, FAKE, 4096, FAKE, need - 1, None) == E_WS
+    assert L.aqd_gemv_grouped(lins(2), 2, 1, FAKE_ODD, 256, FAKE, 1 << 20, None) == E_ALIGN
+    assert L.aqd_gemv_grouped_workspace_bytes(lins(5), 5, 256) == 0

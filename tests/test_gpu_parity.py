@@ -370,3 +370,34 @@ def test_graph_replay_matches_eager(orc):
         torch.cuda.synchronize()
     ref = orc.forward(codes, cb, s, 3, x, lin.block)
     assert normwise(e1.float().cpu().numpy(), ref) <= TOL
+
+
+@pytest.mark.parametrize("shapes,d_in,k", [
+    ([4096, 1024, 1024], 4096, 3),           # q, k, v of the 8B-shaped stack
+    ([14336, 14336], 4096, 2),               # gate, up
+    ([1000, 0, 33, 16], 1000, 2),            # ragged rows and groups, an empty linear, four linears
+])
+def test_grouped_gemv_matches_separate_calls(orc, shapes, d_in, k):
+    """One launch over several linears sharing the input gives, per linear, the bits of its own aqd_gemv
+    call, and the oracle's result within tolerance."""
+    g = wl.rng(91, extra=d_in + sum(shapes))
+    M = 4
+    x = wl.gen_x(g, 1, d_in, "f16")
+    xr = to_dev(x)                                # treated as already rotated
+    lins, refs = [], []
+    for d_out in shapes:
+        codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+        cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+        packed = aqd.aqd_pack_codes(cdev)
+        lins.append((packed, cbdev, sdev, d_out, M))
+        refs.append((codes, cb, s))
+    outs = aqd.aqd_gemv_grouped(lins, k, xr, d_in)
+    for (packed, cbdev, sdev, d_out, _), y, (codes, cb, s) in zip(lins, outs, refs):
+        if d_out == 0:
+            continue
+        single = aqd.aqd_gemv(packed, cbdev, sdev, k, xr, d_out, d_in, M)
+        assert torch.equal(y, single), d_out
+        ref = orc.linear(codes, cb, s, k, x)
+        e = normwise(y.float().cpu().numpy(), ref)
+        record(test="gemv_grouped", d_out=d_out, d_in=d_in, k=k, err=e)
+        assert e <= TOL, (d_out, e)
