@@ -58,6 +58,7 @@ _SIGNATURES = {
     "aqd_gemv": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_gemv_grouped_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_linear), _I32, _I64]),
     "aqd_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _VP, _SZ, _VP]),
+    "aqd_rotate_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
 }
@@ -177,11 +178,12 @@ def aqd_gemv_grouped_workspace_bytes(d_outs, d_in: int, Ms) -> int:
 
 
 def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
-                     workspace: Optional[torch.Tensor] = None):
+                     workspace: Optional[torch.Tensor] = None, block: int = 0):
     """Batch-1 GEMV of several linears sharing x_rot (fp16 [d_in] or [1][d_in]) in one launch.
 
     linears: sequence of (packed, codebooks, scales, d_out, M) or (packed, codebooks, scales, d_out, M, out);
-    returns the fp16 outputs [1][d_out], one per linear.
+    returns the fp16 outputs [1][d_out], one per linear.  With block (64/128/256) the input is the raw
+    activation and the launch applies the block rotation itself (aqd_rotate_gemv_grouped).
     """
     outs, parts = [], []
     for lin in linears:
@@ -193,9 +195,20 @@ def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
     need = int(lib().aqd_gemv_grouped_workspace_bytes(arr, len(parts), d_in))
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
-    _check(lib().aqd_gemv_grouped(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, _ptr(workspace),
-                                  workspace.numel() if workspace is not None else 0, _stream()))
+    nws = workspace.numel() if workspace is not None else 0
+    if block:
+        _check(lib().aqd_rotate_gemv_grouped(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, block,
+                                             _ptr(workspace), nws, _stream()))
+    else:
+        _check(lib().aqd_gemv_grouped(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, _ptr(workspace), nws,
+                                      _stream()))
     return outs
+
+
+def aqd_rotate_gemv_grouped(linears, k: int, x: torch.Tensor, d_in: int, block: int,
+                            workspace: Optional[torch.Tensor] = None):
+    """Rotation (block 64/128/256) of the raw fp16 activation x and the grouped batch-1 GEMV, one launch."""
+    return aqd_gemv_grouped(linears, k, x, d_in, workspace=workspace, block=block)
 
 
 def aqd_gemm_small_batch_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:

@@ -68,8 +68,9 @@ struct LutLinearRef {
 };
 bool gemv_lut_grouped_supported(int64_t G, int k);
 size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n);
+// rotate_block 0: x is already rotated; 64/128/256: x is raw and each workgroup rotates what it needs
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
-                                   void* ws, hipStream_t s);
+                                   void* ws, hipStream_t s, int rotate_block);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,

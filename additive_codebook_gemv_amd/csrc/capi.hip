@@ -168,8 +168,24 @@ size_t aqd_gemv_grouped_workspace_bytes(const aqd_linear* linears, int32_t n_lin
     return gemv_lut_grouped_workspace_bytes(d_out, n_linears);
 }
 
+static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
+                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block);
+
 aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
                             int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
+    return gemv_grouped(linears, n_linears, k, x_rot, d_in, workspace, workspace_bytes, stream, 0);
+}
+
+aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
+                                   int64_t d_in, int32_t block, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    if (block != 64 && block != 128 && block != 256) return fail(AQD_ERR_BLOCK, "block must be 64, 128 or 256");
+    if (d_in % block) return fail(AQD_ERR_BLOCK, "block must divide d_in");
+    return gemv_grouped(linears, n_linears, k, x, d_in, workspace, workspace_bytes, stream, block);
+}
+
+static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
+                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block) {
     aqd_layer layers[AQD_MAX_GROUP];
     aqd_status st = check_group(linears, n_linears, d_in, layers);
     if (st != AQD_OK) return st;
@@ -198,8 +214,9 @@ aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_
     for (int i = 0; i < n_linears; ++i)
         refs[i] = LutLinearRef{linears[i].packed_codes, linears[i].codebooks, linears[i].scales, linears[i].y,
                                linears[i].d_out};
-    return hip_status(launch_gemv_lut_grouped(refs, n_linears, k, x_rot, d_in, workspace, (hipStream_t)stream),
-                      "aqd_gemv_grouped");
+    return hip_status(launch_gemv_lut_grouped(refs, n_linears, k, x_rot, d_in, workspace, (hipStream_t)stream,
+                                              block),
+                      block ? "aqd_rotate_gemv_grouped" : "aqd_gemv_grouped");
 }
 
 size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch) {

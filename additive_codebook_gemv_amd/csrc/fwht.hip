@@ -1,13 +1,8 @@
 // Online block Walsh-Hadamard rotation of the activation (Drop-by-Drop,
 // section 5: block-wise Walsh-Hadamard rotation; applied online at inference).
-//
-// One 64-wide wavefront transforms one block of b inputs.  Lane l holds the
-// elements l, l + 64, l + 128, ... of the block (b/64 per lane), so the six
-// butterfly stages whose partners are 1..32 apart cross lanes and the stages
-// 64 and 128 apart stay in registers.  Sums are fp32; the result is scaled by
-// 1/sqrt(b) and rounded once to the output type.  The butterfly network gives
-// the Sylvester-order matrix H[r][c] = (-1)^popcount(r & c).
-#include "aqd_internal.h"
+// One 64-wide wavefront transforms one block of b inputs (fwht_device.h) and
+// rounds the result once to the output type.
+#include "fwht_device.h"
 
 namespace aqd {
 
@@ -33,11 +28,6 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, int64_t plane
     }
 }
 
-template <int B>
-__device__ __forceinline__ float inv_sqrt_block() {
-    return B == 64 ? 0.125f : (B == 128 ? 0.0883883476483184405f : 0.0625f);
-}
-
 template <int B, int IN, int OUT>
 __global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y,
                                                        int64_t d_in, int64_t n_blocks, int64_t plane) {
@@ -50,29 +40,9 @@ __global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y,
     float v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = load_as_f32<IN>(x, base + e * 64 + lane);
+    fwht_block<B>(v, lane);
 #pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {
-        const bool upper = (lane & h) != 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float o = __shfl_xor(v[e], h);
-            v[e] = upper ? (o - v[e]) : (v[e] + o);
-        }
-    }
-#pragma unroll
-    for (int hb = 1; hb < E; hb <<= 1) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if ((e & hb) == 0) {
-                const float a = v[e], c = v[e | hb];
-                v[e] = a + c;
-                v[e | hb] = a - c;
-            }
-        }
-    }
-    const float sc = inv_sqrt_block<B>();
-#pragma unroll
-    for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e] * sc);
+    for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e]);
 }
 
 template <int B, int IN>

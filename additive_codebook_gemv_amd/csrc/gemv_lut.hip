@@ -32,7 +32,7 @@
 // it by s_i, rounds to fp16, writes y and clears the word.  No barrier or
 // counter is needed, results are bit-reproducible, and the workspace is zero
 // again when the kernel ends.
-#include "aqd_internal.h"
+#include "fwht_device.h"
 
 namespace aqd {
 
@@ -155,9 +155,14 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
     return d;
 }
 
-template <int WAVES, int K, bool MULTI>
+// HB > 0: x is the raw fp16 activation and the workgroup applies the block
+// Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
+// butterflies and rounding of the standalone rotation (same bits).
+template <int WAVES, int K, bool MULTI, int HB>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
-    __shared__ __align__(16) uint8_t lds[LUT_BYTES + 16];
+    constexpr int XS_BYTES = HB > 0 ? LUT_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
+    __shared__ __align__(16) uint8_t lds[LUT_BYTES + XS_BYTES + 16];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + LUT_BYTES);              // [slot][512]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -209,7 +214,27 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
             bok[u][h] = q < p.n_slots && g < p.G;
             const int64_t gc = g < p.G ? g : p.G - 1;
             av[u][h] = *reinterpret_cast<const uint2*>(L.codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
-            bv[u][h] = *reinterpret_cast<const uint2*>(p.x + gc * GROUP + e0);
+            if (HB == 0) bv[u][h] = *reinterpret_cast<const uint2*>(p.x + gc * GROUP + e0);
+        }
+    }
+    // raw activation blocks for the rotation: slot s needs inputs 512*tile .. +512 (tile = q / K),
+    // i.e. 512 / HB blocks; wave w takes blocks w, w + WAVES, ...
+    constexpr int BLK_PER_SLOT = HB > 0 ? TILE_GROUPS * GROUP / HB : 1;
+    constexpr int NBLK = LUT_SLOTS * BLK_PER_SLOT;
+    constexpr int BPW = (NBLK + WAVES - 1) / WAVES;
+    constexpr int E = HB > 0 ? HB / 64 : 1;
+    float xv[BPW][E];
+    bool xok[BPW];
+    if (HB > 0) {
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int blk = wave + b * WAVES;
+            const int sl = (blk < NBLK ? blk : 0) / BLK_PER_SLOT, j = (blk < NBLK ? blk : 0) % BLK_PER_SLOT;
+            const int q = slice * LUT_SLOTS + sl;
+            const int64_t in0 = (int64_t)((q < p.n_slots ? q : 0) / K) * (TILE_GROUPS * GROUP) + (int64_t)j * HB;
+            xok[b] = blk < NBLK && q < p.n_slots && in0 < p.G * GROUP;
+#pragma unroll
+            for (int e = 0; e < E; ++e) xv[b][e] = h2f(p.x[xok[b] ? in0 + e * 64 + lane : lane]);
         }
     }
 
@@ -237,6 +262,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
         row_scale[u] = L.scales[row < L.d_out ? row : L.d_out - 1];
+    }
+    if (HB > 0) {
+#pragma unroll
+        for (int b = 0; b < BPW; ++b) {
+            const int blk = wave + b * WAVES;
+            if (blk >= NBLK) continue;                          // uniform over the wave
+            if constexpr (HB > 0) fwht_block<HB>(xv[b], lane);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xs[blk * HB + e * 64 + lane] = xok[b] ? f2h(xv[b][e]) : (uint16_t)0;
+        }
+        __syncthreads();                                        // rotated inputs of every slot are in LDS
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u) {
+            const int item = wave + u * WAVES;
+            const int gb = item & 1, pair = item >> 4;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                bv[u][h] = *reinterpret_cast<const uint2*>(xs + (2 * pair + h) * (TILE_GROUPS * GROUP) +
+                                                           (gb * 32 + (lane & 31)) * GROUP + 4 * (lane >> 5));
+        }
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
@@ -367,22 +412,22 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
     return b;
 }
 
-template <bool MULTI>
+template <bool MULTI, int HB>
 static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
     switch (k) {
-        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI>), gd, bd, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI>), gd, bd, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI>), gd, bd, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI>), gd, bd, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI>), gd, bd, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI>), gd, bd, 0, s, a); break;
-        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI>), gd, bd, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI>), gd, bd, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB>), gd, bd, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB>), gd, bd, 0, s, a); break;
     }
 }
 
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
-                                   void* ws, hipStream_t s) {
+                                   void* ws, hipStream_t s, int rotate_block) {
     const int64_t G = d_in / GROUP;
     const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
     LutArgs a = {};
@@ -420,15 +465,18 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
         wg += a.slices * blocks[i];
     }
     const dim3 gd((unsigned)wg), bd(64 * LUT_WAVES);
-    if (m == 1) launch_k<false>(k, gd, bd, s, a);
-    else launch_k<true>(k, gd, bd, s, a);
+    if (rotate_block == 64) launch_k<true, 64>(k, gd, bd, s, a);
+    else if (rotate_block == 128) launch_k<true, 128>(k, gd, bd, s, a);
+    else if (rotate_block == 256) launch_k<true, 256>(k, gd, bd, s, a);
+    else if (m == 1) launch_k<false, 0>(k, gd, bd, s, a);
+    else launch_k<true, 0>(k, gd, bd, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                            const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s) {
     const LutLinearRef one = {packed, codebooks, scales, y, g.d_out};
-    return launch_gemv_lut_grouped(&one, 1, k, x, g.d_in, ws, s);
+    return launch_gemv_lut_grouped(&one, 1, k, x, g.d_in, ws, s, 0);
 }
 
 }  // namespace aqd

@@ -104,9 +104,10 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
     """One decode token through the synthetic 32-layer stack of 8B shape (linears and rotations only).
 
     Per layer: q/k/v share one rotated input, o, gate/up (shared) and down get their own; every linear
-    uses the layer's seeded k.  Two schedules of the same work, each captured in one graph and replayed:
-    grouped (q, k, v in one launch, gate and up in one launch: 4 rotations + 4 GEMV launches per layer)
-    and separate (4 rotations + 7 GEMV launches per layer).
+    uses the layer's seeded k.  Three schedules of the same work, each captured in one graph and replayed:
+    fused (each launch rotates its own input; q, k, v in one launch, gate and up in one launch: 4 launches
+    per layer), grouped (4 rotations + 4 GEMV launches per layer) and separate (4 rotations + 7 GEMV
+    launches per layer).
     """
     lins = wl.config(4)
     ks = wl.stack_ks()
@@ -160,6 +161,15 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
                              for j in group for (l, p, c, s_) in [layers[layer * 7 + j]]]
                     aqd.aqd_gemv_grouped(parts, lin0.ks[0], xr, lin0.d_in, workspace=ws)
 
+    def token_fused():
+        for layer in range(32):
+            for group in ((0, 1, 2), (3,), (4, 5), (6,)):
+                lin0 = layers[layer * 7 + group[0]][0]
+                x = inputs[(layer, src[lin0.proj])][0]
+                parts = [(p, c, s_, l.d_out, l.M, outs[layer * 7 + j])
+                         for j in group for (l, p, c, s_) in [layers[layer * 7 + j]]]
+                aqd.aqd_rotate_gemv_grouped(parts, lin0.ks[0], x, lin0.d_in, wl.block_for(lin0.d_in), workspace=ws)
+
     stream = torch.cuda.current_stream()
 
     def timed(token):
@@ -189,19 +199,22 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
         torch.cuda.synchronize()
         return us, a2.elapsed_time(b2) * 1e3 / 3
 
-    us, us_eager = timed(token_grouped)
+    us, us_eager = timed(token_fused)
+    us_grp, us_grp_eager = timed(token_grouped)
     us_sep, us_sep_eager = timed(token_separate)
     return {
         "workload": "32-layer decoder stack of 8B shape (q,o 4096x4096; k,v 1024x4096; gate,up 14336x4096; "
                     "down 4096x14336), batch 1, M=4, per-layer k from {2,3,4} (seeded), linears and rotations "
-                    "only; q/k/v and gate/up grouped into one launch each",
+                    "only; each launch rotates its own input, q/k/v and gate/up grouped into one launch each",
         "layer_k": ks,
-        "launches_per_token": 32 * 8,
+        "launches_per_token": 32 * 4,
         "code_bytes_per_token": code_bytes,
         "us_per_token_graph": us,
         "tokens_per_s_graph": 1e6 / us,
         "us_per_token_eager": us_eager,
         "frac_hbm_peak_graph": code_bytes / us / 1e3 / HBM_PEAK_GBPS,
+        "grouped_rotations_apart": {"launches_per_token": 32 * 8, "us_per_token_graph": us_grp,
+                                    "us_per_token_eager": us_grp_eager},
         "separate_launches": {"launches_per_token": 32 * 11, "us_per_token_graph": us_sep,
                               "us_per_token_eager": us_sep_eager},
     }

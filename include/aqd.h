@@ -190,6 +190,20 @@ aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_
                             int64_t d_in, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Rotation and grouped batch-1 GEMV in one launch.  x is the raw (unrotated)
+ * fp16 activation [d_in]; every workgroup applies the block Walsh-Hadamard
+ * rotation of aqd_hadamard_rotate (block 64, 128 or 256, same butterflies and
+ * fp16 rounding) to the inputs it needs, then proceeds as aqd_gemv_grouped:
+ * the outputs have the bits of aqd_hadamard_rotate (F16 out) followed by
+ * aqd_gemv_grouped (Drop-by-Drop, section 5: the activation is rotated online).
+ * AQD_ERR_BLOCK if block is not 64/128/256 or does not divide d_in; other
+ * arguments, workspace and errors as for aqd_gemv_grouped.
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
+                                   int64_t d_in, int32_t block, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/* ---------------------------------------------------------------------------
  * Small-batch product, batch 1..64, on the matrix cores.  Each wave rebuilds
  * the weight slice its MFMA operand holds from the codes (codeword sums) and
  * multiplies it with 16-column tiles of the rotated activation, accumulating in

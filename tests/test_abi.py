@@ -190,3 +190,8 @@ def test_grouped_gemv_rejects_bad_arguments(L):
     assert L.aqd_gemv_grouped(big, 3, 2, FAKE, 4096, FAKE, need - 1, None) == E_WS
     assert L.aqd_gemv_grouped(lins(2), 2, 1, FAKE_ODD, 256, FAKE, 1 << 20, None) == E_ALIGN
     assert L.aqd_gemv_grouped_workspace_bytes(lins(5), 5, 256) == 0
+    # the fused rotation: block must be 64/128/256 and divide d_in
+    assert L.aqd_rotate_gemv_grouped(lins(2), 2, 1, FAKE, 256, 32, FAKE, 1 << 20, None) == E_BLOCK
+    assert L.aqd_rotate_gemv_grouped(lins(2), 2, 1, FAKE, 192, 128, FAKE, 1 << 20, None) == E_BLOCK
+    assert L.aqd_rotate_gemv_grouped(lins(5), 5, 1, FAKE, 256, 64, FAKE, 1 << 20, None) == E_SHAPE
+    assert L.aqd_rotate_gemv_grouped(big, 3, 2, FAKE, 4096, 128, None, 0, None) == E_WS

@@ -401,3 +401,33 @@ def test_grouped_gemv_matches_separate_calls(orc, shapes, d_in, k):
         e = normwise(y.float().cpu().numpy(), ref)
         record(test="gemv_grouped", d_out=d_out, d_in=d_in, k=k, err=e)
         assert e <= TOL, (d_out, e)
+
+
+@pytest.mark.parametrize("shapes,d_in,block,k", [
+    ([4096, 1024, 1024], 4096, 128, 3),     # q, k, v with their rotation
+    ([4096], 14336, 256, 4),                 # down projection
+    ([300, 17], 576, 64, 2),                 # ragged rows, a partial group tile, block 64
+    ([64], 256, 256, 1),
+])
+def test_rotate_gemv_grouped_matches_rotate_then_gemv(orc, shapes, d_in, block, k):
+    """The launch that rotates its own input gives the bits of the standalone rotation followed by the
+    grouped GEMV, and the oracle's rotate-then-multiply within tolerance."""
+    g = wl.rng(97, extra=d_in + block + sum(shapes))
+    M = 4
+    x = wl.gen_x(g, 1, d_in, "f16")
+    xd = to_dev(x)
+    lins, refs = [], []
+    for d_out in shapes:
+        codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+        cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+        lins.append((aqd.aqd_pack_codes(cdev), cbdev, sdev, d_out, M))
+        refs.append((codes, cb, s))
+    fused = aqd.aqd_rotate_gemv_grouped(lins, k, xd, d_in, block)
+    xr = aqd.aqd_hadamard_rotate(xd, block, aqd.AQD_F16)
+    split = aqd.aqd_gemv_grouped(lins, k, xr, d_in)
+    for y, y2, (codes, cb, s), d_out in zip(fused, split, refs, shapes):
+        assert torch.equal(y, y2), d_out
+        ref = orc.forward(codes, cb, s, k, x, block)
+        e = normwise(y.float().cpu().numpy(), ref)
+        record(test="rotate_gemv_grouped", d_out=d_out, d_in=d_in, block=block, k=k, err=e)
+        assert e <= TOL, (d_out, e)
