@@ -238,8 +238,9 @@ class QuantizedLinear:
     """One additive-codebook linear resident on the GPU: packed codes, codebooks, scales.
 
     ``forward(x, k)`` rotates the activation online and applies the k-codebook
-    product: batch 1..8 through the GEMV (fp16 output), batch 9..64 through the
-    fp16 matrix-core path (fp32 output).
+    product: batch 1 (fp16) in one launch that rotates its own input, batch
+    1..8 through the rotation and the GEMV (fp16 output), batch 9..64 through
+    the fp16 matrix-core path (fp32 output).
     """
 
     def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, block: int):
@@ -256,6 +257,10 @@ class QuantizedLinear:
 
     def forward(self, x: torch.Tensor, k: int) -> torch.Tensor:
         x2 = x.reshape(-1, self.d_in)
+        if x2.shape[0] == 1 and x2.dtype == torch.float16 and self.d_in > 0:
+            # one launch: the GEMV rotates its own input
+            return aqd_rotate_gemv_grouped([(self.packed, self.codebooks, self.scales, self.d_out, self.M)], k,
+                                           x2.contiguous(), self.d_in, self.block, workspace=self.workspace)[0]
         if x2.shape[0] <= 8:
             xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
             return aqd_gemv(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
