@@ -61,6 +61,7 @@ _SIGNATURES = {
     "aqd_rotate_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
+    "aqd_gemm_small_batch_tiered": (_INT, [_VP, _VP, _VP, ctypes.POINTER(_I32), _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
 }
 
 
@@ -231,6 +232,27 @@ def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: 
     _check(lib().aqd_gemm_small_batch(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x_rot), x_dtype,
                                       _ptr(out), batch, ctypes.byref(L), _ptr(workspace),
                                       workspace.numel() if workspace is not None else 0, _stream()))
+    return out
+
+
+def aqd_gemm_small_batch_tiered(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, ks,
+                                x_rot: torch.Tensor, d_out: int, d_in: int, M: int,
+                                out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[batch][d_out] fp32 where column n uses the first ks[n] codebooks; x_rot fp16 [batch][d_in]."""
+    batch = x_rot.shape[0]
+    if len(ks) != batch:
+        raise ValueError("one k per column")
+    L = layer(d_out, d_in, M)
+    if out is None:
+        out = torch.empty((batch, d_out), dtype=torch.float32, device=x_rot.device)
+    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch))
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
+    karr = (ctypes.c_int32 * batch)(*[int(k) for k in ks])
+    _check(lib().aqd_gemm_small_batch_tiered(_ptr(packed), _ptr(codebooks), _ptr(scales), karr, _ptr(x_rot),
+                                             _ptr(out), batch, ctypes.byref(L), _ptr(workspace),
+                                             workspace.numel() if workspace is not None else 0, _stream()))
     return out
 
 

@@ -72,6 +72,10 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n);
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
                                    void* ws, hipStream_t s, int rotate_block);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
+// tiered batch: column n uses the first ks[n] codebooks (host array)
+hipError_t launch_gemm_sb_tiered(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales,
+                                 const int32_t* ks, const uint16_t* x, float* y, int batch, const Geometry& g,
+                                 void* ws, hipStream_t s);
 hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,
                           hipStream_t s);

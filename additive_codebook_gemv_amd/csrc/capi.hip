@@ -241,4 +241,28 @@ aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* cod
                       "aqd_gemm_small_batch");
 }
 
+aqd_status aqd_gemm_small_batch_tiered(const uint8_t* packed_codes, const uint16_t* codebooks,
+                                       const uint16_t* scales, const int32_t* ks, const uint16_t* x_rot,
+                                       float* y, int32_t batch, const aqd_layer* layer,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 1 || batch > 64) return fail(AQD_ERR_SHAPE, "aqd_gemm_small_batch_tiered batch must be in [1, 64]");
+    if (!ks) return fail(AQD_ERR_NULL, "ks is NULL");
+    aqd_status st = check_layer(layer);
+    if (st != AQD_OK) return st;
+    int kmax = 1;
+    for (int n = 0; n < batch; ++n) {
+        if (ks[n] < 1 || ks[n] > layer->M) return fail(AQD_ERR_K, "every ks[n] must be in [1, M]");
+        kmax = ks[n] > kmax ? ks[n] : kmax;
+    }
+    bool nothing = false;
+    const size_t need = aqd_gemm_small_batch_workspace_bytes(layer, batch);
+    st = check_product(packed_codes, codebooks, scales, kmax, x_rot, y, layer, workspace, workspace_bytes, need,
+                       &nothing);
+    if (st != AQD_OK || nothing) return st;
+    if (reinterpret_cast<uintptr_t>(y) % 4) return fail(AQD_ERR_ALIGN, "y must be 4-byte aligned");
+    return hip_status(launch_gemm_sb_tiered(packed_codes, codebooks, scales, ks, x_rot, y, batch, geometry(*layer),
+                                            workspace, (hipStream_t)stream),
+                      "aqd_gemm_small_batch_tiered");
+}
+
 }  // extern "C"

@@ -36,6 +36,16 @@ constexpr int SB_CHUNK_GROUPS = SB_CHUNK / GROUP;
 constexpr int SB_XROW = SB_CHUNK * 2 + 16;         // bytes per activation row in LDS (padded)
 constexpr int SB_MAX_SPLITS = 16;
 
+// Internal operand mode of the tiered batch: fp16 activation, each column n
+// uses its own number of codebooks k_n, one MFMA per codebook plane with the
+// columns that do not use that plane zeroed in the B operand.
+constexpr int SB_MIXED = 100;
+
+// Columns that use codebook m: bit n of cols[m] (n < 64).
+struct SbPlaneCols {
+    unsigned long long cols[MAX_M];
+};
+
 template <int MODE>
 struct XPlanes {
     static constexpr int n = MODE == AQD_BF16X2 ? 2 : 1;
@@ -58,7 +68,8 @@ template <int NT, int MODE, int K>
 __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     const uint8_t* __restrict__ packed, const uint4* __restrict__ codebooks, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ x, float* __restrict__ out, int64_t d_out, int64_t d_in, int64_t G,
-    int64_t n_rt, int64_t plane_bytes, int batch, int chunks_per_split, int64_t n_chunks, int direct) {
+    int64_t n_rt, int64_t plane_bytes, int batch, int chunks_per_split, int64_t n_chunks, int direct,
+    SbPlaneCols pc) {
     constexpr int XP = XPlanes<MODE>::n;
     extern __shared__ __align__(16) uint8_t lds[];
     uint4* cb_lds = reinterpret_cast<uint4*>(lds);                        // [k][256] codewords
@@ -76,6 +87,14 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     const int kq = lane >> 4;     // 8-wide k slot inside the 32-wide MFMA step
 
     for (int i = tid; i < K * CODEWORDS; i += 64 * SB_WAVES) cb_lds[i] = codebooks[i];
+    // tiered batch: the codebooks each of this lane's B columns uses (bit m)
+    uint32_t col_planes[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        col_planes[t] = 0u;
+#pragma unroll
+        for (int m = 0; m < K; ++m) col_planes[t] |= (uint32_t)((pc.cols[m] >> ((t * 16 + r) & 63)) & 1ull) << m;
+    }
 
     // activation chunk staging: thread t moves 16 bytes (8 inputs) of one row of one plane
     constexpr int X_ITEMS = XP * NT * 16 * (SB_CHUNK / 8);   // 16-byte pieces per chunk
@@ -156,6 +175,25 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int64_t j = ch * SB_CHUNK_GROUPS + 4 * s + kq;   // this lane's group
+            if (MODE == SB_MIXED) {
+                // one MFMA per codebook plane; a column that stops before plane m sees zeros there
+                uint4 bx[NT];
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    bx[t] = *reinterpret_cast<const uint4*>(xb + (t * 16 + r) * SB_XROW + (32 * s + 8 * kq) * 2);
+#pragma unroll
+                for (int m = 0; m < K; ++m) {
+                    uint4 c = cb_lds[m * CODEWORDS + cur[m][s]];
+                    if (j >= G) c = make_uint4(0u, 0u, 0u, 0u);
+                    const half8_t a = __builtin_bit_cast(half8_t, c);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const uint4 b = (col_planes[t] >> m) & 1u ? bx[t] : make_uint4(0u, 0u, 0u, 0u);
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, b), acc[t], 0, 0, 0);
+                    }
+                }
+                continue;
+            }
             uint32_t w[4] = {0u, 0u, 0u, 0u};
             if (j < G) {
 #pragma unroll
@@ -302,7 +340,8 @@ size_t gemm_sb_workspace_bytes(const Geometry& g, int batch) {
 
 template <int NT, int MODE, int K>
 static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
-                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
+                           const SbPlaneCols& pc) {
     const SbPlan p = sb_plan(g, sb_per_cu<MODE>(K, batch));
     const int64_t n = (int64_t)batch * g.d_out;
     if (p.n_chunks == 0) {                                   // empty input: Y = 0
@@ -319,7 +358,7 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
     hipLaunchKernelGGL((gemm_sb_kernel<NT, MODE, K>), dim3((unsigned)p.wg_rows, (unsigned)p.splits),
                        dim3(64 * SB_WAVES), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
                        direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
-                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0);
+                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192)),
@@ -329,27 +368,29 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
 
 template <int MODE, int K>
 static hipError_t launch_n(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
-                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
+                           const SbPlaneCols& pc) {
     switch ((batch + 15) / 16) {
-        case 1: return launch_t<1, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 2: return launch_t<2, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 3: return launch_t<3, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
-        default: return launch_t<4, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 1: return launch_t<1, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 2: return launch_t<2, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 3: return launch_t<3, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        default: return launch_t<4, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
     }
 }
 
 template <int MODE>
 static hipError_t launch_m(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
-                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
+                           const SbPlaneCols& pc) {
     switch (k) {
-        case 1: return launch_n<MODE, 1>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 2: return launch_n<MODE, 2>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 3: return launch_n<MODE, 3>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 4: return launch_n<MODE, 4>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 5: return launch_n<MODE, 5>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 6: return launch_n<MODE, 6>(packed, cb, scales, x, y, batch, g, ws, s);
-        case 7: return launch_n<MODE, 7>(packed, cb, scales, x, y, batch, g, ws, s);
-        default: return launch_n<MODE, 8>(packed, cb, scales, x, y, batch, g, ws, s);
+        case 1: return launch_n<MODE, 1>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 2: return launch_n<MODE, 2>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 3: return launch_n<MODE, 3>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 4: return launch_n<MODE, 4>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 5: return launch_n<MODE, 5>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 6: return launch_n<MODE, 6>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 7: return launch_n<MODE, 7>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        default: return launch_n<MODE, 8>(packed, cb, scales, x, y, batch, g, ws, s, pc);
     }
 }
 
@@ -357,9 +398,22 @@ hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, cons
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,
                           hipStream_t s) {
     const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (x_dt == AQD_F16) return launch_m<AQD_F16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
-    if (x_dt == AQD_BF16X2) return launch_m<AQD_BF16X2>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
-    return launch_m<AQD_BF16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s);
+    const SbPlaneCols none = {};
+    if (x_dt == AQD_F16) return launch_m<AQD_F16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
+    if (x_dt == AQD_BF16X2) return launch_m<AQD_BF16X2>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
+    return launch_m<AQD_BF16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
+}
+
+hipError_t launch_gemm_sb_tiered(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales,
+                                 const int32_t* ks, const uint16_t* x, float* y, int batch, const Geometry& g,
+                                 void* ws, hipStream_t s) {
+    SbPlaneCols pc = {};
+    int kmax = 1;
+    for (int n = 0; n < batch; ++n) {
+        kmax = ks[n] > kmax ? ks[n] : kmax;
+        for (int m = 0; m < ks[n]; ++m) pc.cols[m] |= 1ull << n;
+    }
+    return launch_m<SB_MIXED>(packed, codebooks, scales, kmax, x, y, batch, g, ws, s, pc);
 }
 
 }  // namespace aqd

@@ -220,6 +220,50 @@ def measure_stack(aqd, wl, torch, dev, replays: int = 20):
     }
 
 
+def measure_tiered(aqd, wl, torch, dev, copies: int = 32, reps: int = 2):
+    """Tiered batch on the 4096x14336 down projection: 16 requests at k = 4, 3, 2, 1 (four each) in one
+    launch, against the same requests as four single-k launches of four columns each."""
+    lin = [l for l in wl.config(5) if l.name == "down4096x14336_sb"][0]
+    codes, cb, sc, _ = wl.layer_inputs(5, lin, batch=64)
+    packed0 = aqd.aqd_pack_codes(torch.from_numpy(codes).to(dev))
+    cps = [packed0] + [packed0.clone() for _ in range(copies - 1)]
+    cbd, sd = torch.from_numpy(cb).to(dev), torch.from_numpy(sc).to(dev)
+    g = np.random.Generator(np.random.PCG64(0x7E))
+    xr = torch.from_numpy(g.standard_normal((16, lin.d_in)).astype(np.float16)).to(dev)
+    ks = [4] * 4 + [3] * 4 + [2] * 4 + [1] * 4
+    y = torch.empty((16, lin.d_out), dtype=torch.float32, device=dev)
+    ys = [torch.empty((4, lin.d_out), dtype=torch.float32, device=dev) for _ in range(4)]
+    xs = [xr[4 * t:4 * t + 4].contiguous() for t in range(4)]
+    ws = torch.zeros(max(aqd.aqd_gemm_small_batch_workspace_bytes(lin.d_out, lin.d_in, lin.M, 16), 16),
+                     dtype=torch.uint8, device=dev)
+
+    def one(c):
+        aqd.aqd_gemm_small_batch_tiered(cps[c], cbd, sd, ks, xr, lin.d_out, lin.d_in, lin.M, out=y, workspace=ws)
+
+    def split(c):
+        for t, k in enumerate((4, 3, 2, 1)):
+            aqd.aqd_gemm_small_batch(cps[c], cbd, sd, k, xs[t], lin.d_out, lin.d_in, lin.M, aqd.AQD_F16,
+                                     out=ys[t], workspace=ws)
+
+    res = {"workload": "4096x14336, 16 requests: k = 4, 3, 2, 1 for four each, fp16 activations", "ks": ks}
+    for name, fn in (("one_launch", one), ("four_single_k_launches", split)):
+        for c in range(copies):
+            fn(c)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for c in range(copies):
+                fn(c)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (reps * copies)
+        res[name] = {"us": us, "requests_per_s": 16 * 1e6 / us}
+    del cps, packed0
+    torch.cuda.empty_cache()
+    return res
+
+
 def measure_batched_gemv(aqd, torch, dev, copies, cbd, sd, stream, reps: int = 3):
     """The GEMV at batch 2, 4 and 8 on the timed layer (the code stream is read once for all columns),
     k = 1..4, each over a captured graph of back-to-back launches on the cold copies."""
@@ -433,6 +477,7 @@ def main():
     batched = None if args.no_batched else measure_batched_gemv(aqd, torch, dev, copies, cbd, sd, stream)
     stack = None if args.no_stack else measure_stack(aqd, wl, torch, dev)
     small = None if args.no_small_batch else measure_small_batch(aqd, wl, torch, dev)
+    tiered = None if args.no_small_batch else measure_tiered(aqd, wl, torch, dev)
 
     value = float(np.mean([per_k[k]["us_per_gemv"] for k in KS]))
     k4 = per_k[4]
@@ -475,6 +520,8 @@ def main():
         result["stack"] = stack
     if small is not None:
         result["small_batch"] = small
+    if tiered is not None:
+        result["tiered_batch"] = tiered
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, cb, s, x, args.cpu_budget, y_check)
     print(json.dumps(result))

@@ -225,6 +225,26 @@ aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears,
  * ------------------------------------------------------------------------- */
 size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch);
 
+/* ---------------------------------------------------------------------------
+ * Tiered batch: the small-batch product where column n of the batch uses its
+ * own number of codebooks ks[n] (1..M), in one launch.  Each codebook plane m
+ * is read once for all the columns with ks[n] > m; with the planes stored as a
+ * prefix (Drop-by-Drop, section 5: any first k codebooks form a model) a batch
+ * of requests at different bitwidths shares one pass over the codes.
+ *
+ * y[n][i] = s_i * sum_j sum_{m < ks[n]} < C_m[codes[i][j][m]], x_rot[n][8j .. 8j+8) >   (fp32)
+ *
+ * ks:     host array [batch], each 1..M (AQD_ERR_K otherwise), read during the call.
+ * x_rot:  fp16 [batch][d_in] (already rotated).  One fp16 MFMA pass per
+ *         codebook plane, fp32 accumulation.
+ * y, workspace (aqd_gemm_small_batch_workspace_bytes), errors: as for
+ * aqd_gemm_small_batch.
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_gemm_small_batch_tiered(const uint8_t* packed_codes, const uint16_t* codebooks,
+                                       const uint16_t* scales, const int32_t* ks, const uint16_t* x_rot,
+                                       float* y, int32_t batch, const aqd_layer* layer,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* codebooks,
                                 const uint16_t* scales, int32_t k, const void* x_rot, int x_dtype,
                                 float* y, int32_t batch, const aqd_layer* layer,

@@ -116,6 +116,13 @@ def test_small_batch_rejects_bad_arguments(L):
     assert sb(x_dt=F32) == E_DTYPE
     assert sb(y=FAKE + 2) == E_ALIGN
     assert sb(x=None) == E_NULL
+    ks = (ctypes.c_int32 * 16)(*([2] * 8 + [1] * 8))
+    tier = lambda ks_, batch=16: L.aqd_gemm_small_batch_tiered(FAKE, FAKE, FAKE, ks_, FAKE, FAKE, batch, lay(),
+                                                                FAKE, 1 << 30, None)
+    assert tier(None) == E_NULL
+    assert tier((ctypes.c_int32 * 16)(*([3] + [1] * 15))) == E_K        # M = 2
+    assert tier((ctypes.c_int32 * 16)(*([0] + [1] * 15))) == E_K
+    assert tier(ks, batch=65) == E_SHAPE
     big = lay(4096, 14336, 4)
     need = L.aqd_gemm_small_batch_workspace_bytes(big, 16)
     assert need > 0                                   # the input dimension is split over workgroups

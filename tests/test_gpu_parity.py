@@ -431,3 +431,51 @@ def test_rotate_gemv_grouped_matches_rotate_then_gemv(orc, shapes, d_in, block, 
         e = normwise(y.float().cpu().numpy(), ref)
         record(test="rotate_gemv_grouped", d_out=d_out, d_in=d_in, block=block, k=k, err=e)
         assert e <= TOL, (d_out, e)
+
+
+@pytest.mark.parametrize("name,ks", [
+    ("down4096x14336_sb", [4] * 4 + [3] * 4 + [2] * 4 + [1] * 4),          # tiers sorted by descending k
+    ("gate14336x4096_sb", [2, 4, 1, 3] * 8),                               # unsorted, 32 columns
+])
+def test_small_batch_tiered(orc, name, ks):
+    """One launch where column n uses the first ks[n] codebooks: every column matches the oracle at its own k,
+    and the single-k product of its tier within tolerance."""
+    lin = [l for l in wl.config(5) if l.name == name][0]
+    B = len(ks)
+    codes, cb, s, _ = wl.layer_inputs(5, lin, batch=64)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    x = wl.gen_x(wl.rng(101, extra=B), B, lin.d_in, "f16")
+    xd = to_dev(x)                                 # treated as already rotated
+    y = aqd.aqd_gemm_small_batch_tiered(packed, cbdev, sdev, ks, xd, lin.d_out, lin.d_in, lin.M).cpu().numpy()
+    for k in sorted(set(ks)):
+        cols = [n for n in range(B) if ks[n] == k]
+        ref = orc.linear(codes, cb, s, k, x[cols])
+        e = normwise(y[cols], ref)
+        record(test="small_batch_tiered", layer=name, k=k, columns=len(cols), err=e)
+        assert e <= TOL, (k, e)
+        single = aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, xd[cols].contiguous(), lin.d_out, lin.d_in,
+                                          lin.M, aqd.AQD_F16).cpu().numpy()
+        assert normwise(y[cols], single.astype(np.float64)) <= TOL, k
+
+
+def test_small_batch_tiered_edge(orc):
+    d_out, d_in, M = 1000, 1000, 3
+    g = wl.rng(103)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    ks = [3, 1, 2, 3, 1]
+    x = wl.gen_x(g, len(ks), d_in, "f16")
+    y = aqd.aqd_gemm_small_batch_tiered(packed, cbdev, sdev, ks, to_dev(x), d_out, d_in, M).cpu().numpy()
+    for n, k in enumerate(ks):
+        ref = orc.linear(codes, cb, s, k, x[n:n + 1])
+        assert normwise(y[n:n + 1], ref) <= TOL, (n, k)
+    # dyadic inputs: exact in any summation order, so the tiered product is bit-exact against the oracle
+    codes, cb, s, xq = wl.dyadic_case(wl.rng(105), 200, 512, 2, batch=8)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    ks = [2, 1, 1, 2, 2, 1, 2, 1]
+    y = aqd.aqd_gemm_small_batch_tiered(packed, cbdev, sdev, ks, to_dev(xq), 200, 512, 2).cpu().numpy()
+    for n, k in enumerate(ks):
+        assert np.array_equal(y[n].astype(np.float64), orc.linear(codes, cb, s, k, xq[n:n + 1])[0]), n
