@@ -259,15 +259,23 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     }
 }
 
-// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i]
-__global__ void sb_reduce_kernel(const float* __restrict__ part, const uint16_t* __restrict__ scales,
-                                 float* __restrict__ y, int64_t d_out, int batch, int splits) {
+// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i].  Column n
+// is blockIdx.y; all the splits' partials are requested before any is added.
+__global__ __launch_bounds__(256) void sb_reduce_kernel(const float* __restrict__ part,
+                                                        const uint16_t* __restrict__ scales, float* __restrict__ y,
+                                                        int64_t d_out, int batch, int splits) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i >= d_out) return;
+    const int64_t e = (int64_t)blockIdx.y * d_out + i;
     const int64_t n = (int64_t)batch * d_out;
-    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
-        float v = 0.f;
-        for (int sp = 0; sp < splits; ++sp) v += part[(int64_t)sp * n + e];
-        y[e] = h2f(scales[e % d_out]) * v;
-    }
+    float v[SB_MAX_SPLITS];
+#pragma unroll
+    for (int sp = 0; sp < SB_MAX_SPLITS; ++sp) v[sp] = part[(sp < splits ? sp : 0) * n + e];
+    float acc = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < SB_MAX_SPLITS; ++sp)
+        if (sp < splits) acc += v[sp];
+    y[e] = h2f(scales[i]) * acc;
 }
 
 __global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
@@ -361,8 +369,8 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                        p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192)),
-                       dim3(256), 0, s, static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits);
+    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((g.d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
+                       static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits);
     return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@
 // it by s_i, rounds to fp16, writes y and clears the word.  No barrier or
 // counter is needed, results are bit-reproducible, and the workspace is zero
 // again when the kernel ends.
+#include "fixed_sum.h"
 #include "fwht_device.h"
 
 namespace aqd {
@@ -89,24 +90,8 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t code_dword, uint32_t base,
     return __builtin_amdgcn_perm(code_dword, base, 0x0C020000u | ((uint32_t)(4 + byte) << 8));
 }
 
-// Row sums travel between workgroups in one 64-bit word per row: the top 8
-// bits count the contributions, the low 56 bits hold the sum of the
-// contributions as fixed point with 24 fraction bits, each biased by 2^47 so
-// that every term is non-negative and no carry reaches the count (at most 255
-// terms below 2^48 each).  Integer addition makes the total exact and
-// independent of arrival order; the adder that sees S-1 earlier contributions
-// in the returned word holds the complete sum.
-constexpr int FIX_FRAC = 24;
-constexpr int FIX_COUNT_SHIFT = 56;
-constexpr unsigned long long FIX_BIAS = 1ull << 47;
-constexpr double FIX_LIMIT = (double)((1ll << 47) - 1);
-constexpr int LUT_MAX_SLICES = 255;
-
-__device__ __forceinline__ unsigned long long fix_term(float v) {
-    double d = (double)v * (double)(1 << FIX_FRAC);
-    d = d > FIX_LIMIT ? FIX_LIMIT : (d < -FIX_LIMIT ? -FIX_LIMIT : d);
-    return (unsigned long long)(__double2ll_rn(d) + (long long)FIX_BIAS);
-}
+// Row sums travel between workgroups as counted fixed-point words (fixed_sum.h).
+constexpr int LUT_MAX_SLICES = FIX_MAX_TERMS;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -356,18 +341,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         if ((lane & 3) == 0 && row < L.d_out) {
             mine[u] = true;
             term[u] = fix_term(sum);
-            old_word[u] = atomicAdd(L.acc + row, (1ull << FIX_COUNT_SHIFT) + term[u]);
+            old_word[u] = atomicAdd(L.acc + row, fix_add_word(term[u]));
         }
     }
 #pragma unroll
     for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
-        if (!mine[u] || (int)(old_word[u] >> FIX_COUNT_SHIFT) != p.slices - 1) continue;
+        if (!mine[u] || !fix_is_last(old_word[u], p.slices)) continue;
         // this lane added the last contribution of its row: it holds the complete sum
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
         if (row >= L.d_out) continue;
-        const unsigned long long biased = (old_word[u] & ((1ull << FIX_COUNT_SHIFT) - 1)) + term[u];
-        const long long total = (long long)biased - (long long)p.slices * (long long)FIX_BIAS;
-        L.y[row] = f2h(h2f(row_scale[u]) * (float)((double)total * (1.0 / (double)(1 << FIX_FRAC))));
+        L.y[row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], p.slices));
         __hip_atomic_store(L.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }

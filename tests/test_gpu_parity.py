@@ -479,3 +479,4 @@ def test_small_batch_tiered_edge(orc):
     y = aqd.aqd_gemm_small_batch_tiered(packed, cbdev, sdev, ks, to_dev(xq), 200, 512, 2).cpu().numpy()
     for n, k in enumerate(ks):
         assert np.array_equal(y[n].astype(np.float64), orc.linear(codes, cb, s, k, xq[n:n + 1])[0]), n
+
