@@ -62,6 +62,8 @@ class Oracle:
         lib.oracle_encode.argtypes = [_c_dp, ctypes.c_int, _i64, _c_u16p]
         lib.oracle_hadamard.argtypes = [_i32, _c_i32p]
         lib.oracle_rotate.argtypes = [_c_dp, _i64, _i64, _i32, _c_dp]
+        lib.oracle_sign_vector.argtypes = [_c_u8p, _i64, _c_dp]
+        lib.oracle_rotate_signed.argtypes = [_c_dp, _c_u8p, _i64, _i64, _i32, _c_dp]
         lib.oracle_reconstruct.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp]
         lib.oracle_linear.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp, _i64, _c_dp]
         lib.oracle_forward.argtypes = [_c_u8p, _c_dp, _c_dp, _i64, _i64, _i32, _i32, _c_dp, _i64, _i32, _c_dp]
@@ -120,6 +122,26 @@ class Oracle:
         rc = self.lib.oracle_rotate(_ptr(xd, _c_dp), xd.shape[0], xd.shape[1], b, _ptr(out, _c_dp))
         if rc != 0:
             raise ValueError(f"oracle_rotate rc={rc}")
+        return out
+
+    def sign_vector(self, signs: np.ndarray, d_in: int) -> np.ndarray:
+        """+-1.0 per input from the sign bit mask (bit c % 8 of byte c // 8 set -> -1)."""
+        signs = np.ascontiguousarray(signs, dtype=np.uint8)
+        assert signs.size * 8 >= d_in
+        eps = np.empty(d_in, dtype=np.float64)
+        assert self.lib.oracle_sign_vector(_ptr(signs, _c_u8p), d_in, _ptr(eps, _c_dp)) == 0
+        return eps
+
+    def rotate_signed(self, x: np.ndarray, signs: np.ndarray, b: int, dtype: str = "f16") -> np.ndarray:
+        """Randomized rotation H_b diag(eps) / sqrt(b) per block of x [B][d_in] (float64 result)."""
+        xd = np.ascontiguousarray(np.atleast_2d(self._f64(x, dtype)))
+        signs = np.ascontiguousarray(signs, dtype=np.uint8)
+        assert signs.size * 8 >= xd.shape[1]
+        out = np.empty_like(xd)
+        rc = self.lib.oracle_rotate_signed(_ptr(xd, _c_dp), _ptr(signs, _c_u8p), xd.shape[0], xd.shape[1], b,
+                                           _ptr(out, _c_dp))
+        if rc != 0:
+            raise ValueError(f"oracle_rotate_signed rc={rc}")
         return out
 
     def reconstruct(self, codes: np.ndarray, codebooks: np.ndarray, scales: Optional[np.ndarray], k: int) -> np.ndarray:

@@ -30,7 +30,8 @@
  *   - the scale multiplies the whole output row and one scale serves every k;
  *   - the rotation is orthonormal: H_b / sqrt(b) with H_b the Sylvester
  *     (natural-order) Walsh-Hadamard matrix, H[r][c] = (-1)^popcount(r & c),
- *     applied to contiguous aligned blocks of b inputs, no random signs;
+ *     applied to contiguous aligned blocks of b inputs, no random signs
+ *     (the signed variant below is a separate entry, R = H_b diag(eps)/sqrt(b));
  *   - codeword element t multiplies input 8j + t.
  *
  * Everything here is the definition written out: the Hadamard product is a
@@ -227,6 +228,65 @@ int oracle_rotate(const double *x, int64_t batch, int64_t d_in, int32_t b, doubl
         }
     }
     free(H);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
+ * Randomized block Hadamard rotation R = (1/sqrt(b)) H_b diag(eps), the
+ * variant of "ApexQuant: calibration-free elastic quantization" (section 3,
+ * the randomized Hadamard transform named after Eq. 2).  The sign pattern is a
+ * bit mask: eps_c = -1 when bit (c mod 8) of byte signs[c / 8] is set, +1
+ * otherwise; one pattern serves every row of the batch.
+ * ------------------------------------------------------------------------- */
+
+/* eps[c] = -1.0 or +1.0 from the bit mask, c in [0, d_in). */
+int oracle_sign_vector(const uint8_t *signs, int64_t d_in, double *eps)
+{
+    if (d_in < 0 || (d_in > 0 && !signs))
+        return -1;
+    for (int64_t c = 0; c < d_in; ++c)
+        eps[c] = ((signs[c / 8] >> (c % 8)) & 1u) ? -1.0 : 1.0;
+    return 0;
+}
+
+/* out[n][beta*b + r] = b^(-1/2) * sum_c H[r][c] * eps[beta*b + c] * x[n][beta*b + c]
+ * x, out: [batch][d_in] doubles; b must divide d_in.  Dense product per block. */
+int oracle_rotate_signed(const double *x, const uint8_t *signs, int64_t batch, int64_t d_in, int32_t b,
+                         double *out)
+{
+    if (!valid_block(b) || d_in % b != 0 || batch < 0)
+        return -1;
+    int32_t *H = (int32_t *)malloc(sizeof(int32_t) * (size_t)b * (size_t)b);
+    double *eps = (double *)malloc(sizeof(double) * (size_t)(d_in > 0 ? d_in : 1));
+    if (!H || !eps) {
+        free(H);
+        free(eps);
+        return -2;
+    }
+    oracle_hadamard(b, H);
+    if (oracle_sign_vector(signs, d_in, eps) != 0) {
+        free(H);
+        free(eps);
+        return -1;
+    }
+    const double inv = 1.0 / sqrt((double)b);
+    const int64_t nblk = d_in / b;
+    int64_t t;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < batch * nblk; ++t) {
+        const int64_t n = t / nblk, beta = t % nblk;
+        const double *xs = x + n * d_in + beta * b;
+        const double *es = eps + beta * b;
+        double *os = out + n * d_in + beta * b;
+        for (int32_t r = 0; r < b; ++r) {
+            double acc = 0.0;
+            for (int32_t c = 0; c < b; ++c)
+                acc += (double)H[(int64_t)r * b + c] * (es[c] * xs[c]);
+            os[r] = acc * inv;
+        }
+    }
+    free(H);
+    free(eps);
     return 0;
 }
 

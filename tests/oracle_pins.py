@@ -190,6 +190,71 @@ def pin_rotation_invariance(orc):
         assert np.allclose(WQt @ Qx[0], W @ x[0], rtol=1e-12, atol=1e-12)
 
 
+def _np_eps(signs: np.ndarray, d_in: int) -> np.ndarray:
+    """Independent sign expansion with numpy's little-endian bit unpacking: bit c % 8 of byte c // 8."""
+    bits = np.unpackbits(np.asarray(signs, dtype=np.uint8), bitorder="little")[:d_in]
+    return 1.0 - 2.0 * bits.astype(np.float64)
+
+
+def pin_sign_mask_layout(orc):
+    """Worked by hand: bytes 0x05, 0x80 flip inputs 0, 2 and 15; every other input keeps its sign."""
+    eps = orc.sign_vector(np.array([0x05, 0x80, 0x00], dtype=np.uint8), 24)
+    want = np.ones(24)
+    want[[0, 2, 15]] = -1.0
+    assert np.array_equal(eps, want), eps
+
+
+def pin_signed_rotation_special_cases(orc):
+    """No bits set is the unsigned rotation; every bit set negates it; one bit negates one input."""
+    g = _rng(6)
+    for b in (64, 128, 256):
+        d = 2 * b
+        x = g.standard_normal((2, d))
+        zero = np.zeros(d // 8, dtype=np.uint8)
+        full = np.full(d // 8, 0xFF, dtype=np.uint8)
+        assert np.array_equal(orc.rotate_signed(x, zero, b), orc.rotate(x, b))
+        assert np.array_equal(orc.rotate_signed(x, full, b), -orc.rotate(x, b))
+        for c in (0, 7, b + 9, d - 1):
+            one = zero.copy()
+            one[c // 8] = 1 << (c % 8)
+            xf = x.copy()
+            xf[:, c] = -xf[:, c]
+            assert np.allclose(orc.rotate_signed(x, one, b), _np_blockdiag_rotate(xf, b), rtol=0, atol=1e-12), c
+
+
+def pin_signed_rotation_closed_forms(orc):
+    """R = H diag(eps)/sqrt(b): R e_c = eps_c H[:, c]/sqrt(b); R^T R = I; Q (R x) = eps * x."""
+    g = _rng(7)
+    for b in (64, 128, 256):
+        d = 2 * b
+        signs = g.integers(0, 256, d // 8, dtype=np.uint8)
+        eps = _np_eps(signs, d)
+        H = _sylvester(b).astype(np.float64)
+        R = orc.rotate_signed(np.eye(d), signs, b).T          # column c = R e_c
+        for c in range(d):
+            blk, cc = divmod(c, b)
+            want = np.zeros(d)
+            want[blk * b:(blk + 1) * b] = eps[c] * H[:, cc] / np.sqrt(b)
+            assert np.allclose(R[:, c], want, rtol=0, atol=1e-15), (b, c)
+        assert np.allclose(R.T @ R, np.eye(d), rtol=0, atol=1e-13)
+        x = g.standard_normal((3, d))
+        assert np.allclose(orc.rotate(orc.rotate_signed(x, signs, b), b), x * eps, rtol=0, atol=1e-12)
+        assert np.allclose(orc.rotate_signed(x, signs, b), _np_blockdiag_rotate(x * eps, b), rtol=0, atol=1e-12)
+
+
+def pin_signed_rotation_invariance(orc):
+    """W x = (W R^T)(R x): rotating the weight rows by R cancels the randomized activation rotation."""
+    g = _rng(8)
+    for b in (64, 256):
+        d_in = 2 * b
+        signs = g.integers(0, 256, d_in // 8, dtype=np.uint8)
+        W = g.standard_normal((7, d_in))
+        x = g.standard_normal((1, d_in))
+        WRt = orc.rotate_signed(W, signs, b)   # row i of W R^T is R w_i
+        Rx = orc.rotate_signed(x, signs, b)
+        assert np.allclose(WRt @ Rx[0], W @ x[0], rtol=1e-12, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # reconstruction and product
 # ---------------------------------------------------------------------------

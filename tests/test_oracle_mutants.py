@@ -23,6 +23,11 @@ MUTANTS = {
     "rotation_no_normalisation": ("ob[r] = acc * inv;", "ob[r] = acc;"),
     "rotation_wrong_input_index": ("H[(int64_t)r * b + c] * xb[c];", "H[(int64_t)r * b + c] * xb[r];"),
     "rotation_block_offset_dropped": ("const double *xb = x + n * d_in + beta * b;", "const double *xb = x + n * d_in;"),
+    "signed_eps_ignored": ("acc += (double)H[(int64_t)r * b + c] * (es[c] * xs[c]);",
+                           "acc += (double)H[(int64_t)r * b + c] * (xs[c]);"),
+    "sign_bits_msb_first": ("eps[c] = ((signs[c / 8] >> (c % 8)) & 1u)", "eps[c] = ((signs[c / 8] >> (7 - c % 8)) & 1u)"),
+    "sign_block_offset_dropped": ("const double *es = eps + beta * b;", "const double *es = eps;"),
+    "signed_no_normalisation": ("os[r] = acc * inv;", "os[r] = acc;"),
     "first_codebook_dropped": ("for (int32_t m = 0; m < k; ++m) {", "for (int32_t m = 1; m < k; ++m) {"),
     "prefix_ignored": ("for (int32_t m = 0; m < k; ++m) {", "for (int32_t m = 0; m < M; ++m) {"),
     "planes_reversed": ("const uint8_t c = codes[(i * G + j) * M + m];", "const uint8_t c = codes[(i * G + j) * M + (M - 1 - m)];"),
