@@ -54,11 +54,14 @@ _SIGNATURES = {
     "aqd_pack_codes": (_INT, [_VP, _VP, _LP, _VP]),
     "aqd_unpack_codes": (_INT, [_VP, _VP, _LP, _VP]),
     "aqd_hadamard_rotate": (_INT, [_VP, _VP, _INT, _INT, _I64, _I64, _I32, _VP]),
+    "aqd_hadamard_rotate_signed": (_INT, [_VP, _VP, _INT, _INT, _I64, _I64, _I32, _VP, _VP]),
     "aqd_gemv_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemv": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_gemv_grouped_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_linear), _I32, _I64]),
     "aqd_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _VP, _SZ, _VP]),
     "aqd_rotate_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _SZ, _VP]),
+    "aqd_rotate_gemv_grouped_signed": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _VP,
+                                              _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_tiered": (_INT, [_VP, _VP, _VP, ctypes.POINTER(_I32), _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
@@ -126,19 +129,36 @@ def aqd_unpack_codes(packed: torch.Tensor, d_out: int, d_in: int, M: int,
     return out
 
 
+def _rotation_out(x2: torch.Tensor, out_dtype: int) -> torch.Tensor:
+    batch, d_in = x2.shape
+    if out_dtype == AQD_BF16X2:
+        return torch.empty((2, batch, d_in), dtype=torch.bfloat16, device=x2.device)
+    tdt = {AQD_F16: torch.float16, AQD_BF16: torch.bfloat16, AQD_F32: torch.float32}[out_dtype]
+    return torch.empty((batch, d_in), dtype=tdt, device=x2.device)
+
+
 def aqd_hadamard_rotate(x: torch.Tensor, block: int, out_dtype: int = AQD_F16,
                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """x: [batch][d_in] fp16/bf16/fp32 -> rotated [batch][d_in] (or [2][batch][d_in] for AQD_BF16X2)."""
     x2 = x.reshape(-1, x.shape[-1])
     batch, d_in = x2.shape
     if out is None:
-        if out_dtype == AQD_BF16X2:
-            out = torch.empty((2, batch, d_in), dtype=torch.bfloat16, device=x.device)
-        else:
-            tdt = {AQD_F16: torch.float16, AQD_BF16: torch.bfloat16, AQD_F32: torch.float32}[out_dtype]
-            out = torch.empty((batch, d_in), dtype=tdt, device=x.device)
+        out = _rotation_out(x2, out_dtype)
     _check(lib().aqd_hadamard_rotate(_ptr(x2), _ptr(out), _TORCH_DT[x.dtype], out_dtype, batch, d_in, block,
                                      _stream()))
+    return out
+
+
+def aqd_hadamard_rotate_signed(x: torch.Tensor, block: int, signs: torch.Tensor, out_dtype: int = AQD_F16,
+                               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Randomized rotation H diag(eps) / sqrt(b) per block; signs: uint8 [d_in / 8] device bit mask
+    (bit c % 8 of byte c // 8 set -> input c negated)."""
+    x2 = x.reshape(-1, x.shape[-1])
+    batch, d_in = x2.shape
+    if out is None:
+        out = _rotation_out(x2, out_dtype)
+    _check(lib().aqd_hadamard_rotate_signed(_ptr(x2), _ptr(out), _TORCH_DT[x.dtype], out_dtype, batch, d_in,
+                                            block, _ptr(signs), _stream()))
     return out
 
 
@@ -179,12 +199,14 @@ def aqd_gemv_grouped_workspace_bytes(d_outs, d_in: int, Ms) -> int:
 
 
 def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
-                     workspace: Optional[torch.Tensor] = None, block: int = 0):
+                     workspace: Optional[torch.Tensor] = None, block: int = 0,
+                     signs: Optional[torch.Tensor] = None):
     """Batch-1 GEMV of several linears sharing x_rot (fp16 [d_in] or [1][d_in]) in one launch.
 
     linears: sequence of (packed, codebooks, scales, d_out, M) or (packed, codebooks, scales, d_out, M, out);
     returns the fp16 outputs [1][d_out], one per linear.  With block (64/128/256) the input is the raw
-    activation and the launch applies the block rotation itself (aqd_rotate_gemv_grouped).
+    activation and the launch applies the block rotation itself (aqd_rotate_gemv_grouped), with the sign
+    mask of the randomized rotation when signs is given (aqd_rotate_gemv_grouped_signed).
     """
     outs, parts = [], []
     for lin in linears:
@@ -197,7 +219,12 @@ def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
     if need and workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
     nws = workspace.numel() if workspace is not None else 0
-    if block:
+    if signs is not None:
+        if not block:
+            raise ValueError("signs apply to the rotating launch only (give block)")
+        _check(lib().aqd_rotate_gemv_grouped_signed(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, block,
+                                                    _ptr(signs), _ptr(workspace), nws, _stream()))
+    elif block:
         _check(lib().aqd_rotate_gemv_grouped(arr, len(parts), k, _ptr(x_rot.reshape(-1)), d_in, block,
                                              _ptr(workspace), nws, _stream()))
     else:
@@ -210,6 +237,12 @@ def aqd_rotate_gemv_grouped(linears, k: int, x: torch.Tensor, d_in: int, block: 
                             workspace: Optional[torch.Tensor] = None):
     """Rotation (block 64/128/256) of the raw fp16 activation x and the grouped batch-1 GEMV, one launch."""
     return aqd_gemv_grouped(linears, k, x, d_in, workspace=workspace, block=block)
+
+
+def aqd_rotate_gemv_grouped_signed(linears, k: int, x: torch.Tensor, d_in: int, block: int, signs: torch.Tensor,
+                                   workspace: Optional[torch.Tensor] = None):
+    """As aqd_rotate_gemv_grouped with the randomized rotation H diag(eps) / sqrt(b) (uint8 sign mask)."""
+    return aqd_gemv_grouped(linears, k, x, d_in, workspace=workspace, block=block, signs=signs)
 
 
 def aqd_gemm_small_batch_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:
@@ -262,12 +295,18 @@ class QuantizedLinear:
     ``forward(x, k)`` rotates the activation online and applies the k-codebook
     product: batch 1 (fp16) in one launch that rotates its own input, batch
     1..8 through the rotation and the GEMV (fp16 output), batch 9..64 through
-    the fp16 matrix-core path (fp32 output).
+    the fp16 matrix-core path (fp32 output).  With ``signs`` the rotation is
+    the randomized H diag(eps) / sqrt(b), and the codes must be those of W R^T.
     """
 
-    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, block: int):
+    def __init__(self, codes: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, block: int,
+                 signs: Optional[torch.Tensor] = None):
         d_out, G, M = codes.shape
         self.d_out, self.d_in, self.M, self.block = d_out, G * 8, M, block
+        # randomized rotation H diag(eps) when a sign mask (uint8 [d_in / 8]) is given
+        self.signs = None if signs is None else signs.contiguous()
+        if self.signs is not None and (self.signs.dtype != torch.uint8 or self.signs.numel() * 8 != self.d_in):
+            raise ValueError("signs must be uint8 [d_in / 8]")
         self.packed = aqd_pack_codes(codes)
         self.codebooks = codebooks.contiguous()
         self.scales = scales.contiguous()
@@ -277,16 +316,22 @@ class QuantizedLinear:
         if n:
             self.workspace = torch.zeros(n, dtype=torch.uint8, device=codes.device)
 
+    def rotate(self, x2: torch.Tensor) -> torch.Tensor:
+        """fp16 rotated activation (with the sign mask when the layer has one)."""
+        if self.signs is not None:
+            return aqd_hadamard_rotate_signed(x2, self.block, self.signs, AQD_F16)
+        return aqd_hadamard_rotate(x2, self.block, AQD_F16)
+
     def forward(self, x: torch.Tensor, k: int) -> torch.Tensor:
         x2 = x.reshape(-1, self.d_in)
         if x2.shape[0] == 1 and x2.dtype == torch.float16 and self.d_in > 0:
             # one launch: the GEMV rotates its own input
-            return aqd_rotate_gemv_grouped([(self.packed, self.codebooks, self.scales, self.d_out, self.M)], k,
-                                           x2.contiguous(), self.d_in, self.block, workspace=self.workspace)[0]
+            return aqd_gemv_grouped([(self.packed, self.codebooks, self.scales, self.d_out, self.M)], k,
+                                    x2.contiguous(), self.d_in, workspace=self.workspace, block=self.block,
+                                    signs=self.signs)[0]
+        xr = self.rotate(x2)
         if x2.shape[0] <= 8:
-            xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
             return aqd_gemv(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
                             workspace=self.workspace)
-        xr = aqd_hadamard_rotate(x2, self.block, AQD_F16)
         return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
                                     AQD_F16, workspace=self.workspace)

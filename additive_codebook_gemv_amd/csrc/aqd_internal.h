@@ -49,8 +49,10 @@ void set_error(const std::string& s);
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, const Geometry& g, hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, uint8_t* codes, const Geometry& g, hipStream_t s);
+// signs: NULL, or a bit mask of d_in bits (8-byte aligned) that negates input c
+// before the butterflies when bit c % 8 of byte c / 8 is set
 hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in,
-                           int block, hipStream_t s);
+                           int block, const uint8_t* signs, hipStream_t s);
 size_t gemv_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
@@ -70,7 +72,7 @@ bool gemv_lut_grouped_supported(int64_t G, int k);
 size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n);
 // rotate_block 0: x is already rotated; 64/128/256: x is raw and each workgroup rotates what it needs
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
-                                   void* ws, hipStream_t s, int rotate_block);
+                                   void* ws, hipStream_t s, int rotate_block, const uint8_t* signs);
 size_t gemm_sb_workspace_bytes(const Geometry& g, int batch);
 // tiered batch: column n uses the first ks[n] codebooks (host array)
 hipError_t launch_gemm_sb_tiered(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales,

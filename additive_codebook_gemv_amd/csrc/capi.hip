@@ -89,8 +89,11 @@ aqd_status aqd_unpack_codes(const uint8_t* packed, uint8_t* codes, const aqd_lay
     return hip_status(launch_unpack(packed, codes, g, (hipStream_t)stream), "aqd_unpack_codes");
 }
 
-aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype, int64_t batch,
-                               int64_t d_in, int32_t block, void* stream) {
+static bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+static aqd_status hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype, int64_t batch,
+                                  int64_t d_in, int32_t block, const uint8_t* signs, bool want_signs,
+                                  void* stream, const char* name) {
     if (in_dtype != AQD_F16 && in_dtype != AQD_BF16 && in_dtype != AQD_F32)
         return fail(AQD_ERR_DTYPE, "in_dtype must be F16, BF16 or F32");
     if (out_dtype != AQD_F16 && out_dtype != AQD_BF16 && out_dtype != AQD_F32 && out_dtype != AQD_BF16X2)
@@ -102,11 +105,26 @@ aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out
     if (d_in % block != 0) return fail(AQD_ERR_BLOCK, "block must divide d_in");
     if (batch * d_in == 0) return AQD_OK;
     if (!x || !x_rot) return fail(AQD_ERR_NULL, "x or x_rot is NULL");
+    if (want_signs && !signs) return fail(AQD_ERR_NULL, "signs is NULL");
     if (!aligned16(x) || !aligned16(x_rot)) return fail(AQD_ERR_ALIGN, "x and x_rot must be 16-byte aligned");
+    if (want_signs && !aligned8(signs)) return fail(AQD_ERR_ALIGN, "signs must be 8-byte aligned");
     if (x == x_rot && (in_dtype != out_dtype || out_dtype == AQD_BF16X2))
         return fail(AQD_ERR_DTYPE, "in-place rotation needs equal in/out dtypes");
-    return hip_status(launch_hadamard(x, x_rot, in_dtype, out_dtype, batch, d_in, block, (hipStream_t)stream),
-                      "aqd_hadamard_rotate");
+    return hip_status(launch_hadamard(x, x_rot, in_dtype, out_dtype, batch, d_in, block,
+                                      want_signs ? signs : nullptr, (hipStream_t)stream),
+                      name);
+}
+
+aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype, int64_t batch,
+                               int64_t d_in, int32_t block, void* stream) {
+    return hadamard_rotate(x, x_rot, in_dtype, out_dtype, batch, d_in, block, nullptr, false, stream,
+                           "aqd_hadamard_rotate");
+}
+
+aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, int out_dtype, int64_t batch,
+                                      int64_t d_in, int32_t block, const uint8_t* signs, void* stream) {
+    return hadamard_rotate(x, x_rot, in_dtype, out_dtype, batch, d_in, block, signs, true, stream,
+                           "aqd_hadamard_rotate_signed");
 }
 
 size_t aqd_gemv_workspace_bytes(const aqd_layer* layer, int32_t batch) {
@@ -169,11 +187,13 @@ size_t aqd_gemv_grouped_workspace_bytes(const aqd_linear* linears, int32_t n_lin
 }
 
 static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
-                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block);
+                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block,
+                               const uint8_t* signs, const char* name);
 
 aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
                             int64_t d_in, void* workspace, size_t workspace_bytes, void* stream) {
-    return gemv_grouped(linears, n_linears, k, x_rot, d_in, workspace, workspace_bytes, stream, 0);
+    return gemv_grouped(linears, n_linears, k, x_rot, d_in, workspace, workspace_bytes, stream, 0, nullptr,
+                        "aqd_gemv_grouped");
 }
 
 aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
@@ -181,11 +201,24 @@ aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears,
                                    void* stream) {
     if (block != 64 && block != 128 && block != 256) return fail(AQD_ERR_BLOCK, "block must be 64, 128 or 256");
     if (d_in % block) return fail(AQD_ERR_BLOCK, "block must divide d_in");
-    return gemv_grouped(linears, n_linears, k, x, d_in, workspace, workspace_bytes, stream, block);
+    return gemv_grouped(linears, n_linears, k, x, d_in, workspace, workspace_bytes, stream, block, nullptr,
+                        "aqd_rotate_gemv_grouped");
+}
+
+aqd_status aqd_rotate_gemv_grouped_signed(const aqd_linear* linears, int32_t n_linears, int32_t k,
+                                          const uint16_t* x, int64_t d_in, int32_t block, const uint8_t* signs,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (block != 64 && block != 128 && block != 256) return fail(AQD_ERR_BLOCK, "block must be 64, 128 or 256");
+    if (d_in % block) return fail(AQD_ERR_BLOCK, "block must divide d_in");
+    if (d_in > 0 && !signs) return fail(AQD_ERR_NULL, "signs is NULL");
+    if (d_in > 0 && !aligned8(signs)) return fail(AQD_ERR_ALIGN, "signs must be 8-byte aligned");
+    return gemv_grouped(linears, n_linears, k, x, d_in, workspace, workspace_bytes, stream, block, signs,
+                        "aqd_rotate_gemv_grouped_signed");
 }
 
 static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x_rot,
-                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block) {
+                               int64_t d_in, void* workspace, size_t workspace_bytes, void* stream, int block,
+                               const uint8_t* signs, const char* name) {
     aqd_layer layers[AQD_MAX_GROUP];
     aqd_status st = check_group(linears, n_linears, d_in, layers);
     if (st != AQD_OK) return st;
@@ -215,8 +248,8 @@ static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int
         refs[i] = LutLinearRef{linears[i].packed_codes, linears[i].codebooks, linears[i].scales, linears[i].y,
                                linears[i].d_out};
     return hip_status(launch_gemv_lut_grouped(refs, n_linears, k, x_rot, d_in, workspace, (hipStream_t)stream,
-                                              block),
-                      block ? "aqd_rotate_gemv_grouped" : "aqd_gemv_grouped");
+                                              block, signs),
+                      name);
 }
 
 size_t aqd_gemm_small_batch_workspace_bytes(const aqd_layer* layer, int32_t batch) {

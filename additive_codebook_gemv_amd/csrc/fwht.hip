@@ -1,7 +1,10 @@
 // Online block Walsh-Hadamard rotation of the activation (Drop-by-Drop,
 // section 5: block-wise Walsh-Hadamard rotation; applied online at inference).
 // One 64-wide wavefront transforms one block of b inputs (fwht_device.h) and
-// rounds the result once to the output type.
+// rounds the result once to the output type.  With a sign mask the inputs are
+// first multiplied by eps = +-1 (the randomized Hadamard transform
+// H diag(eps) of ApexQuant, section 3); a negation is exact, so the result is
+// the unsigned rotation of the sign-flipped input, bit for bit.
 #include "fwht_device.h"
 
 namespace aqd {
@@ -29,50 +32,59 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, int64_t plane
 }
 
 template <int B, int IN, int OUT>
-__global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y,
+__global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y, const uint64_t* signs,
                                                        int64_t d_in, int64_t n_blocks, int64_t plane) {
     constexpr int E = B / 64;
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (wave >= n_blocks) return;
     const int64_t per_row = d_in / B;
-    const int64_t base = (wave / per_row) * d_in + (wave % per_row) * B;
+    const int64_t col = (wave % per_row) * B;                  // first input of the block in its row
+    const int64_t base = (wave / per_row) * d_in + col;
     float v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) v[e] = load_as_f32<IN>(x, base + e * 64 + lane);
+    if (signs) {                                               // uniform: bit `lane` of word (col + 64e) / 64
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if ((signs[col / 64 + e] >> lane) & 1ull) v[e] = -v[e];
+    }
     fwht_block<B>(v, lane);
 #pragma unroll
     for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e]);
 }
 
 template <int B, int IN>
-static hipError_t launch_out(const void* x, void* y, int out_dt, int64_t batch, int64_t d_in, hipStream_t s) {
+static hipError_t launch_out(const void* x, void* y, const uint64_t* sg, int out_dt, int64_t batch, int64_t d_in,
+                             hipStream_t s) {
     const int64_t n_blocks = batch * (d_in / B);
     const int64_t plane = batch * d_in;
     const dim3 grid((unsigned)((n_blocks + 3) / 4)), block(256);
     switch (out_dt) {
-        case AQD_F16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F16>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
-        case AQD_BF16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
-        case AQD_F32: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F32>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
-        default: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16X2>), grid, block, 0, s, x, y, d_in, n_blocks, plane); break;
+        case AQD_F16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F16>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
+        case AQD_BF16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
+        case AQD_F32: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F32>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
+        default: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16X2>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
     }
     return hipGetLastError();
 }
 
 template <int B>
-static hipError_t launch_in(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in, hipStream_t s) {
+static hipError_t launch_in(const void* x, void* y, const uint64_t* sg, int in_dt, int out_dt, int64_t batch,
+                            int64_t d_in, hipStream_t s) {
     switch (in_dt) {
-        case AQD_F16: return launch_out<B, AQD_F16>(x, y, out_dt, batch, d_in, s);
-        case AQD_BF16: return launch_out<B, AQD_BF16>(x, y, out_dt, batch, d_in, s);
-        default: return launch_out<B, AQD_F32>(x, y, out_dt, batch, d_in, s);
+        case AQD_F16: return launch_out<B, AQD_F16>(x, y, sg, out_dt, batch, d_in, s);
+        case AQD_BF16: return launch_out<B, AQD_BF16>(x, y, sg, out_dt, batch, d_in, s);
+        default: return launch_out<B, AQD_F32>(x, y, sg, out_dt, batch, d_in, s);
     }
 }
 
 hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in, int block,
-                           hipStream_t s) {
-    if (block == 64) return launch_in<64>(x, y, in_dt, out_dt, batch, d_in, s);
-    if (block == 128) return launch_in<128>(x, y, in_dt, out_dt, batch, d_in, s);
-    return launch_in<256>(x, y, in_dt, out_dt, batch, d_in, s);
+                           const uint8_t* signs, hipStream_t s) {
+    const uint64_t* sg = reinterpret_cast<const uint64_t*>(signs);
+    if (block == 64) return launch_in<64>(x, y, sg, in_dt, out_dt, batch, d_in, s);
+    if (block == 128) return launch_in<128>(x, y, sg, in_dt, out_dt, batch, d_in, s);
+    return launch_in<256>(x, y, sg, in_dt, out_dt, batch, d_in, s);
 }
 
 }  // namespace aqd

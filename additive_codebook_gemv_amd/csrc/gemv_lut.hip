@@ -66,6 +66,7 @@ struct LutArgs {
     const uint16_t* x;
     int64_t G, n_gt;
     int k, n_slots, slices, n_lin;
+    const uint64_t* signs;       // rotating launch only: NULL or the input sign mask (bit c of word c / 64)
 };
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -142,7 +143,8 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
 
 // HB > 0: x is the raw fp16 activation and the workgroup applies the block
 // Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
-// butterflies and rounding of the standalone rotation (same bits).
+// butterflies and rounding of the standalone rotation (same bits), after the
+// optional sign flips of the randomized variant.
 template <int WAVES, int K, bool MULTI, int HB>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     constexpr int XS_BYTES = HB > 0 ? LUT_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
@@ -220,6 +222,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
             xok[b] = blk < NBLK && q < p.n_slots && in0 < p.G * GROUP;
 #pragma unroll
             for (int e = 0; e < E; ++e) xv[b][e] = h2f(p.x[xok[b] ? in0 + e * 64 + lane : lane]);
+            if (p.signs) {                                      // randomized rotation: eps = -1 where the bit is set
+#pragma unroll
+                for (int e = 0; e < E; ++e)
+                    if ((p.signs[xok[b] ? in0 / 64 + e : 0] >> lane) & 1ull) xv[b][e] = -xv[b][e];
+            }
         }
     }
 
@@ -410,11 +417,12 @@ static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
 }
 
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
-                                   void* ws, hipStream_t s, int rotate_block) {
+                                   void* ws, hipStream_t s, int rotate_block, const uint8_t* signs) {
     const int64_t G = d_in / GROUP;
     const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
     LutArgs a = {};
     a.x = x;
+    a.signs = rotate_block ? reinterpret_cast<const uint64_t*>(signs) : nullptr;
     a.G = G;
     a.n_gt = n_gt;
     a.k = k;
@@ -459,7 +467,7 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                            const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s) {
     const LutLinearRef one = {packed, codebooks, scales, y, g.d_out};
-    return launch_gemv_lut_grouped(&one, 1, k, x, g.d_in, ws, s, 0);
+    return launch_gemv_lut_grouped(&one, 1, k, x, g.d_in, ws, s, 0, nullptr);
 }
 
 }  // namespace aqd

@@ -118,7 +118,8 @@ aqd_status aqd_unpack_codes(const uint8_t* packed, uint8_t* codes, const aqd_lay
  *
  * x_rot[n][beta*b + r] = (1/sqrt(b)) * sum_c H_b[r][c] * x[n][beta*b + c],
  * H_b[r][c] = (-1)^popcount(r & c) (Sylvester order), blocks of b contiguous
- * inputs starting at input 0, no sign flips.  Computed in fp32 by butterflies,
+ * inputs starting at input 0, no sign flips (aqd_hadamard_rotate_signed adds
+ * them).  Computed in fp32 by butterflies,
  * then rounded once to out_dtype.
  *
  * x:      [batch][d_in] in in_dtype (AQD_F16, AQD_BF16 or AQD_F32).
@@ -130,6 +131,27 @@ aqd_status aqd_unpack_codes(const uint8_t* packed, uint8_t* codes, const aqd_lay
  * ------------------------------------------------------------------------- */
 aqd_status aqd_hadamard_rotate(const void* x, void* x_rot, int in_dtype, int out_dtype,
                                int64_t batch, int64_t d_in, int32_t block, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Randomized block rotation R = (1/sqrt(b)) * H_b * diag(eps) per block: the
+ * randomized Hadamard transform H diag(eps) named in "ApexQuant:
+ * calibration-free elastic quantization", section 3 (after Eq. 2), applied
+ * with the block layout of aqd_hadamard_rotate.  The weights it pairs with are
+ * quantized from W R^T, so that (W R^T)(R x) = W x.
+ *
+ * signs:  device bit mask of d_in bits, one pattern for every batch row:
+ *         eps_c = -1 when bit (c mod 8) of byte signs[c / 8] is set, else +1
+ *         (the same memory read as little-endian 64-bit words: bit c mod 64 of
+ *         word c / 64).  d_in / 8 bytes, 8-byte aligned, caller-owned.
+ * Each input is negated (exactly) where its bit is set and the result is then
+ * bit-identical to aqd_hadamard_rotate of the sign-flipped input.  Other
+ * arguments, aliasing rules and errors as for aqd_hadamard_rotate, plus
+ * AQD_ERR_NULL for a NULL signs and AQD_ERR_ALIGN for a misaligned one (when
+ * batch * d_in > 0).
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, int out_dtype,
+                                      int64_t batch, int64_t d_in, int32_t block, const uint8_t* signs,
+                                      void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode GEMV, batch 1..8 (the lookup-and-accumulate hot path).
@@ -202,6 +224,19 @@ aqd_status aqd_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_
 aqd_status aqd_rotate_gemv_grouped(const aqd_linear* linears, int32_t n_linears, int32_t k, const uint16_t* x,
                                    int64_t d_in, int32_t block, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * As aqd_rotate_gemv_grouped with the randomized rotation of
+ * aqd_hadamard_rotate_signed: the outputs have the bits of
+ * aqd_hadamard_rotate_signed (F16 out, same signs) followed by
+ * aqd_gemv_grouped.  signs: d_in / 8 bytes, 8-byte aligned device memory, the
+ * bit layout of aqd_hadamard_rotate_signed; AQD_ERR_NULL / AQD_ERR_ALIGN when
+ * d_in > 0 and it is NULL / misaligned.  Other arguments and errors as for
+ * aqd_rotate_gemv_grouped.
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_rotate_gemv_grouped_signed(const aqd_linear* linears, int32_t n_linears, int32_t k,
+                                          const uint16_t* x, int64_t d_in, int32_t block, const uint8_t* signs,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Small-batch product, batch 1..64, on the matrix cores.  Each wave rebuilds

@@ -146,6 +146,20 @@ def test_hadamard_rejects_bad_arguments(L):
     assert rot(y=FAKE, i=F16, o=BF16X2) == E_DTYPE
 
 
+def test_signed_hadamard_rejects_bad_arguments(L):
+    def rot(x=FAKE, y=FAKE + 4096, i=F16, o=F16, batch=1, d_in=256, b=64, signs=FAKE + 8192):
+        return L.aqd_hadamard_rotate_signed(x, y, i, o, batch, d_in, b, signs, None)
+    assert rot(signs=None) == E_NULL
+    assert rot(signs=FAKE + 8192 + 4) == E_ALIGN          # the mask is read as 64-bit words
+    assert rot(b=32) == E_BLOCK
+    assert rot(b=128, d_in=192) == E_BLOCK
+    assert rot(i=BF16X2) == E_DTYPE
+    assert rot(x=None) == E_NULL
+    assert rot(y=FAKE_ODD) == E_ALIGN
+    assert rot(y=FAKE, i=F16, o=F32) == E_DTYPE
+    assert rot(batch=0, signs=None) == OK                 # nothing to rotate
+
+
 def test_pack_rejects_bad_arguments(L):
     assert L.aqd_pack_codes(FAKE, None, lay(), None) == E_NULL
     assert L.aqd_pack_codes(FAKE, FAKE_ODD, lay(), None) == E_ALIGN
@@ -202,3 +216,11 @@ def test_grouped_gemv_rejects_bad_arguments(L):
     assert L.aqd_rotate_gemv_grouped(lins(2), 2, 1, FAKE, 192, 128, FAKE, 1 << 20, None) == E_BLOCK
     assert L.aqd_rotate_gemv_grouped(lins(5), 5, 1, FAKE, 256, 64, FAKE, 1 << 20, None) == E_SHAPE
     assert L.aqd_rotate_gemv_grouped(big, 3, 2, FAKE, 4096, 128, None, 0, None) == E_WS
+    # the randomized rotation adds a sign mask: required, 8-byte aligned
+    sg = FAKE + 8192
+    assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 1, FAKE, 256, 64, None, FAKE, 1 << 20, None) == E_NULL
+    assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 1, FAKE, 256, 64, sg + 2, FAKE, 1 << 20, None) == E_ALIGN
+    assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 1, FAKE, 256, 32, sg, FAKE, 1 << 20, None) == E_BLOCK
+    assert L.aqd_rotate_gemv_grouped_signed(lins(5), 5, 1, FAKE, 256, 64, sg, FAKE, 1 << 20, None) == E_SHAPE
+    assert L.aqd_rotate_gemv_grouped_signed(big, 3, 2, FAKE, 4096, 128, sg, None, 0, None) == E_WS
+    assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 3, FAKE, 256, 64, sg, FAKE, 1 << 20, None) == E_K

@@ -105,6 +105,45 @@ def test_rotation_bf16_input_and_in_place(orc):
     assert np.all(np.abs(t.cpu().numpy().astype(np.float64) - orc.rotate(xf, 64)) <= _f16_ulp(orc.rotate(xf, 64)))
 
 
+def _eps(signs: np.ndarray, d_in: int) -> np.ndarray:
+    return 1.0 - 2.0 * np.unpackbits(signs, bitorder="little")[:d_in].astype(np.float64)
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_signed_rotation_matches_oracle(orc, block):
+    """H diag(eps) / sqrt(b): the oracle's randomized rotation within rounding, and the bits of the
+    unsigned rotation of the sign-flipped input (a negation is exact)."""
+    d_in = 14336 if block == 256 else 4096
+    g = wl.rng(15, extra=block)
+    x = wl.gen_x(g, 4, d_in, "f16")
+    signs = wl.gen_signs(g, d_in)
+    xd, sd = to_dev(x), to_dev(signs)
+    ref = orc.rotate_signed(x, signs, block)
+    f32 = aqd.aqd_hadamard_rotate_signed(xd, block, sd, aqd.AQD_F32).cpu().numpy()
+    err32 = normwise(f32, ref)
+    assert err32 < 1e-6, err32
+    f16 = aqd.aqd_hadamard_rotate_signed(xd, block, sd, aqd.AQD_F16)
+    assert np.all(np.abs(f16.cpu().numpy().astype(np.float64) - ref) <= _f16_ulp(ref))
+    flipped = to_dev((x.astype(np.float64) * _eps(signs, d_in)).astype(np.float16))
+    assert torch.equal(f16, aqd.aqd_hadamard_rotate(flipped, block, aqd.AQD_F16))
+    zero = torch.zeros_like(sd)
+    assert torch.equal(aqd.aqd_hadamard_rotate_signed(xd, block, zero, aqd.AQD_F16),
+                       aqd.aqd_hadamard_rotate(xd, block, aqd.AQD_F16))
+    t = xd.clone()
+    aqd.aqd_hadamard_rotate_signed(t, block, sd, aqd.AQD_F16, out=t)        # in place
+    assert torch.equal(t, f16)
+    record(test="signed_rotation", block=block, err_f32=err32)
+
+
+@pytest.mark.parametrize("block", [64, 256])
+def test_signed_rotation_bit_exact_on_integers(orc, block):
+    g = wl.rng(16, extra=block)
+    x = g.integers(-8, 9, size=(3, 4 * block)).astype(np.float16)
+    signs = wl.gen_signs(g, 4 * block)
+    got = aqd.aqd_hadamard_rotate_signed(to_dev(x), block, to_dev(signs), aqd.AQD_F16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, orc.encode(orc.rotate_signed(x, signs, block), "f16"))
+
+
 # ---------------------------------------------------------------------------
 # GEMV (batch 1..8)
 # ---------------------------------------------------------------------------
@@ -431,6 +470,54 @@ def test_rotate_gemv_grouped_matches_rotate_then_gemv(orc, shapes, d_in, block, 
         e = normwise(y.float().cpu().numpy(), ref)
         record(test="rotate_gemv_grouped", d_out=d_out, d_in=d_in, block=block, k=k, err=e)
         assert e <= TOL, (d_out, e)
+
+
+@pytest.mark.parametrize("shapes,d_in,block,k", [
+    ([4096, 1024, 1024], 4096, 128, 4),     # q, k, v
+    ([4096], 14336, 256, 2),                 # down projection
+    ([300, 17], 576, 64, 3),                 # ragged rows, a partial group tile
+])
+def test_rotate_gemv_grouped_signed(orc, shapes, d_in, block, k):
+    """Randomized rotation inside the launch: the bits of the signed standalone rotation followed by the
+    grouped GEMV, and the oracle's signed rotation then product within tolerance."""
+    g = wl.rng(98, extra=d_in + block + sum(shapes))
+    M = 4
+    x = wl.gen_x(g, 1, d_in, "f16")
+    signs = wl.gen_signs(g, d_in)
+    xd, sd = to_dev(x), to_dev(signs)
+    lins, refs = [], []
+    for d_out in shapes:
+        codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+        cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+        lins.append((aqd.aqd_pack_codes(cdev), cbdev, sdev, d_out, M))
+        refs.append((codes, cb, s))
+    fused = aqd.aqd_rotate_gemv_grouped_signed(lins, k, xd, d_in, block, sd)
+    xr = aqd.aqd_hadamard_rotate_signed(xd, block, sd, aqd.AQD_F16)
+    split = aqd.aqd_gemv_grouped(lins, k, xr, d_in)
+    xrot = orc.rotate_signed(x, signs, block)
+    for y, y2, (codes, cb, s), d_out in zip(fused, split, refs, shapes):
+        assert torch.equal(y, y2), d_out
+        ref = orc.linear(codes, cb, s, k, xrot)
+        e = normwise(y.float().cpu().numpy(), ref)
+        record(test="rotate_gemv_grouped_signed", d_out=d_out, d_in=d_in, block=block, k=k, err=e)
+        assert e <= TOL, (d_out, e)
+
+
+def test_quantized_linear_signed(orc):
+    """A layer with a sign mask: batch 1 (one launch), batch 4 (GEMV) and batch 16 (matrix cores)."""
+    g = wl.rng(99)
+    d_out, d_in, M, block, k = 512, 1024, 4, 128, 3
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    signs = wl.gen_signs(g, d_in)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    ql = aqd.QuantizedLinear(cdev, cbdev, sdev, block, signs=to_dev(signs))
+    for batch in (1, 4, 16):
+        x = wl.gen_x(g, batch, d_in, "f16")
+        y = ql.forward(to_dev(x), k).float().cpu().numpy()
+        ref = orc.linear(codes, cb, s, k, orc.rotate_signed(x, signs, block))
+        e = normwise(y, ref)
+        record(test="quantized_linear_signed", batch=batch, err=e)
+        assert e <= TOL, (batch, e)
 
 
 @pytest.mark.parametrize("name,ks", [

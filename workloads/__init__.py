@@ -65,6 +65,11 @@ def gen_scales(g: np.random.Generator, d_out: int, lo: float = 0.5, hi: float = 
     return g.uniform(lo, hi, size=d_out).astype(np.float16)
 
 
+def gen_signs(g: np.random.Generator, d_in: int) -> np.ndarray:
+    """Sign bit mask of a randomized rotation: d_in / 8 uniformly random bytes (each bit a fair coin)."""
+    return g.integers(0, 256, size=d_in // 8, dtype=np.uint8)
+
+
 def gen_x(g: np.random.Generator, batch: int, d_in: int, dtype: str = "f16") -> np.ndarray:
     """Activations N(0,1): fp16 array for 'f16', uint16 bf16 bit patterns for 'bf16'."""
     v = g.standard_normal((batch, d_in))
