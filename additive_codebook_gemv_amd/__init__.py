@@ -60,6 +60,8 @@ _SIGNATURES = {
     "aqd_gemv_grouped_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_linear), _I32, _I64]),
     "aqd_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _VP, _SZ, _VP]),
     "aqd_rotate_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _SZ, _VP]),
+    "aqd_gemm_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_layer), _I32]),
+    "aqd_gemm_prefill": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, ctypes.POINTER(aqd_layer), _VP, _SZ, _VP]),
     "aqd_rotate_gemv_grouped_signed": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _VP,
                                               _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
@@ -268,6 +270,30 @@ def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: 
     return out
 
 
+AQD_PREFILL_MAX_BATCH = 32768
+
+
+def aqd_gemm_prefill_workspace_bytes(d_out: int, d_in: int, M: int, batch: int) -> int:
+    return int(lib().aqd_gemm_prefill_workspace_bytes(ctypes.byref(layer(d_out, d_in, M)), batch))
+
+
+def aqd_gemm_prefill(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, k: int,
+                     x_rot: torch.Tensor, d_out: int, d_in: int, M: int, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[batch][d_out] fp32 = s * (W_k @ x_rot) for fp16 x_rot [batch][d_in], batch 1..32768 (meant for >= 128)."""
+    batch = x_rot.shape[0]
+    L = layer(d_out, d_in, M)
+    if out is None:
+        out = torch.empty((batch, d_out), dtype=torch.float32, device=x_rot.device)
+    need = int(lib().aqd_gemm_prefill_workspace_bytes(ctypes.byref(L), batch))
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_rot.device)
+    _check(lib().aqd_gemm_prefill(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x_rot), _ptr(out), batch,
+                                  ctypes.byref(L), _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                                  _stream()))
+    return out
+
+
 def aqd_gemm_small_batch_tiered(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, ks,
                                 x_rot: torch.Tensor, d_out: int, d_in: int, M: int,
                                 out: Optional[torch.Tensor] = None,
@@ -295,7 +321,8 @@ class QuantizedLinear:
     ``forward(x, k)`` rotates the activation online and applies the k-codebook
     product: batch 1 (fp16) in one launch that rotates its own input, batch
     1..8 through the rotation and the GEMV (fp16 output), batch 9..64 through
-    the fp16 matrix-core path (fp32 output).  With ``signs`` the rotation is
+    the fp16 matrix-core path (fp32 output), larger batches (prefill) through
+    the fused dequantize + matrix-core GEMM (fp32 output).  With ``signs`` the rotation is
     the randomized H diag(eps) / sqrt(b), and the codes must be those of W R^T.
     """
 
@@ -333,5 +360,7 @@ class QuantizedLinear:
         if x2.shape[0] <= 8:
             return aqd_gemv(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
                             workspace=self.workspace)
-        return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M,
-                                    AQD_F16, workspace=self.workspace)
+        if x2.shape[0] <= 64:
+            return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in,
+                                        self.M, AQD_F16, workspace=self.workspace)
+        return aqd_gemm_prefill(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M)

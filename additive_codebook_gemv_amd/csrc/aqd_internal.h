@@ -82,6 +82,15 @@ hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, cons
                           const void* x, int x_dt, float* y, int batch, const Geometry& g, void* ws,
                           hipStream_t s);
 
+// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i]; at most 16 splits
+hipError_t launch_split_reduce(const float* part, const uint16_t* scales, float* y, int64_t d_out, int batch,
+                               int splits, hipStream_t s);
+hipError_t launch_zero_f32(float* y, int64_t n, hipStream_t s);
+// prefill / large batch (fp16 activations, fp32 output)
+size_t gemm_pf_workspace_bytes(const Geometry& g, int batch);
+hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                          const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s);
+
 // ---- device helpers --------------------------------------------------------
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 

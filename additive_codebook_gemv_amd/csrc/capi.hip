@@ -298,4 +298,25 @@ aqd_status aqd_gemm_small_batch_tiered(const uint8_t* packed_codes, const uint16
                       "aqd_gemm_small_batch_tiered");
 }
 
+size_t aqd_gemm_prefill_workspace_bytes(const aqd_layer* layer, int32_t batch) {
+    if (check_layer(layer) != AQD_OK || batch < 1 || batch > AQD_PREFILL_MAX_BATCH) return 0;
+    return gemm_pf_workspace_bytes(geometry(*layer), batch);
+}
+
+aqd_status aqd_gemm_prefill(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales,
+                            int32_t k, const uint16_t* x_rot, float* y, int32_t batch, const aqd_layer* layer,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (batch < 1 || batch > AQD_PREFILL_MAX_BATCH)
+        return fail(AQD_ERR_SHAPE, "aqd_gemm_prefill batch must be in [1, AQD_PREFILL_MAX_BATCH]");
+    bool nothing = false;
+    const size_t need = layer ? aqd_gemm_prefill_workspace_bytes(layer, batch) : 0;
+    aqd_status st = check_product(packed_codes, codebooks, scales, k, x_rot, y, layer, workspace, workspace_bytes,
+                                  need, &nothing);
+    if (st != AQD_OK || nothing) return st;
+    if (reinterpret_cast<uintptr_t>(y) % 4) return fail(AQD_ERR_ALIGN, "y must be 4-byte aligned");
+    return hip_status(launch_gemm_pf(packed_codes, codebooks, scales, k, x_rot, y, batch, geometry(*layer),
+                                     workspace, (hipStream_t)stream),
+                      "aqd_gemm_prefill");
+}
+
 }  // extern "C"

@@ -1,0 +1,307 @@
+// Prefill / large-batch product on the matrix cores (batch up to 32768).
+//
+// Same operation as the other paths (Drop-by-Drop, section 3.2: a weight group
+// is the sum of the codewords its codes pick; section 5: only the first k
+// codebooks are used), at batch sizes where the work is a compute-bound dense
+// contraction:  Y[n][i] = s_i * sum_c W_k[i][c] * X[n][c].
+//
+// Workgroup: 4 waves.  Wave w owns 64 weight rows (four 16-row A fragments of
+// v_mfma_f32_16x16x32_f16) and every one of the workgroup's 16*NB batch
+// columns, so a weight row is rebuilt exactly once per workgroup and the
+// accumulators (4 x NB fragments) stay in registers for the whole input range.
+// Per 64-input chunk:
+//   - the activation chunk (16*NB columns x 64 inputs, fp16) is copied into
+//     LDS by direct global-to-LDS loads (no registers), double buffered, with
+//     an XOR swizzle so the 16 lanes that read one B fragment row hit 16
+//     different bank groups;
+//   - the chunk's code bytes (16 row tiles x 8 groups x k planes, 128
+//     contiguous bytes per tile and plane) are copied the same way;
+//   - a lane's A-operand slot (row r of the fragment, 8 consecutive inputs) is
+//     exactly one code group, and the 64 slots of a fragment are 64
+//     consecutive bytes of a packed code tile: one conflict-free byte read per
+//     plane.  The lane adds its k codewords (LDS-resident codebooks) with
+//     packed fp16 adds;
+//   - each A fragment meets all NB B fragments: 4*NB MFMAs per 32 inputs.
+// When the tiles cannot fill the chip the input dimension is split; each split
+// writes fp32 partials to the workspace and the small-batch reduce adds them in
+// a fixed order, so results are bit-reproducible.
+#include "aqd_internal.h"
+
+namespace aqd {
+
+typedef _Float16 pf_half8_t __attribute__((ext_vector_type(8)));
+typedef float pf_floatx4_t __attribute__((ext_vector_type(4)));
+
+constexpr int PF_WAVES = 4;
+constexpr int PF_FRAGS = 4;                              // 16-row A fragments per wave
+constexpr int PF_TILES = PF_WAVES * PF_FRAGS;            // 16-row code tiles per workgroup (256 rows)
+constexpr int PF_CHUNK = 64;                             // inputs per staged chunk (8 groups)
+constexpr int PF_CHUNK_GROUPS = PF_CHUNK / GROUP;
+constexpr int PF_MAX_SPLITS = 16;
+
+struct PfArgs {
+    const uint8_t* packed;
+    const uint4* codebooks;
+    const uint16_t* scales;
+    const uint16_t* x;
+    float* out;
+    int64_t d_out, d_in, G, n_rt, plane_bytes, n_chunks;
+    int batch, chunks_per_split, direct;
+};
+
+__device__ __forceinline__ half2_t pf_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ uint32_t pf_u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+typedef __attribute__((address_space(3))) void pf_lds_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes dst + 16 * l (dst is uniform over the wave).
+__device__ __forceinline__ void pf_dma16(const void* src, uint8_t* dst) {
+    __builtin_amdgcn_global_load_lds(src, (pf_lds_t*)dst, 16, 0, 0);
+}
+
+// Activation slot of (column, 8-input piece) inside a chunk buffer: columns of
+// 128 bytes, the eight 16-byte pieces XOR-swizzled by bits 1..3 of the column,
+// so the 16 columns a B fragment reads at one piece fall in 16 bank groups.
+__device__ __forceinline__ int pf_xslot(int col, int piece) {
+    return col * (PF_CHUNK * 2) + ((piece ^ ((col >> 1) & 7)) << 4);
+}
+
+// LDS of one workgroup.  Each buffer is its own object, so the compiler can see
+// that the copies in flight into one buffer never alias the reads of the other
+// (and of the codebooks) and does not wait for them.
+template <int K, int NB>
+struct PfLds {
+    static constexpr int XB = NB * 16 * PF_CHUNK * 2;                     // activations: NB*16 columns x 128 B
+    static constexpr int CB = K * PF_TILES * PF_CHUNK_GROUPS * TILE_ROWS; // codes: [K][PF_TILES][8 groups][16]
+};
+
+template <int K, int NB>
+__global__ __launch_bounds__(64 * PF_WAVES) void gemm_pf_kernel(PfArgs p) {
+    using L = PfLds<K, NB>;
+    __shared__ __align__(16) uint4 cb_lds[K * CODEWORDS];                 // [K][256] codewords
+    __shared__ __align__(16) uint8_t x0[L::XB];
+    __shared__ __align__(16) uint8_t x1[L::XB];
+    __shared__ __align__(16) uint8_t k0[L::CB];
+    __shared__ __align__(16) uint8_t k1[L::CB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int r = lane & 15;      // A: row in the fragment; B: column in the fragment
+    const int kq = lane >> 4;     // 8-input slot inside a 32-input MFMA step
+    const int64_t rtb = (int64_t)blockIdx.x * PF_TILES;                    // first row tile of the workgroup
+    const int col0 = blockIdx.y * NB * 16;
+    const int64_t c0 = (int64_t)blockIdx.z * p.chunks_per_split;
+    const int64_t c1 = c0 + p.chunks_per_split < p.n_chunks ? c0 + p.chunks_per_split : p.n_chunks;
+
+    for (int i = tid; i < K * CODEWORDS; i += 64 * PF_WAVES) cb_lds[i] = p.codebooks[i];
+
+    // Staging of chunk `ch` into (xd, kd), straight from global memory to LDS.
+    // Activations: one wave instruction moves 8 columns (1 KiB); lane l takes
+    // column l/8 and slot l%8 of them.  Pieces past the batch, past d_in or in
+    // the padding chunk after this split are written as zeros instead
+    // (ordinary LDS stores, only in ragged chunks).
+    // Codes: one wave instruction moves 8 row tiles x 8 groups of one plane.
+    auto stage = [&](int64_t ch, uint8_t* xd, uint8_t* kd) {
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+            const int blk = q * PF_WAVES + wave;                           // 8-column block
+            const int col = blk * 8 + (lane >> 3);
+            const int piece = (lane & 7) ^ ((col >> 1) & 7);
+            const int64_t kk = ch * PF_CHUNK + piece * GROUP;
+            uint8_t* dst = xd + blk * 1024;
+            if (col0 + col < p.batch && kk < p.d_in && ch < c1)
+                pf_dma16(p.x + (int64_t)(col0 + col) * p.d_in + kk, dst);
+            else
+                *reinterpret_cast<uint4*>(dst + lane * 16) = make_uint4(0u, 0u, 0u, 0u);
+        }
+        const int64_t chc = ch < p.n_chunks ? ch : p.n_chunks - 1;        // the trailing padding chunk
+        const int64_t jt = chc / (TILE_GROUPS / PF_CHUNK_GROUPS);
+        const int g0 = (int)(chc % (TILE_GROUPS / PF_CHUNK_GROUPS)) * PF_CHUNK_GROUPS;
+#pragma unroll
+        for (int q = 0; q < (2 * K + PF_WAVES - 1) / PF_WAVES; ++q) {
+            const int idx = q * PF_WAVES + wave;                           // (plane, half of the tiles)
+            if (idx >= 2 * K) break;                                       // uniform over the wave
+            const int m = idx >> 1;
+            const int f = (idx & 1) * 8 + (lane >> 3);
+            const int64_t rt = rtb + f < p.n_rt ? rtb + f : p.n_rt - 1;    // rows past the layer: never stored
+            pf_dma16(p.packed + m * p.plane_bytes + (jt * p.n_rt + rt) * TILE_BYTES + (g0 + (lane & 7)) * TILE_ROWS,
+                     kd + idx * 1024);
+        }
+    };
+
+    pf_floatx4_t acc[PF_FRAGS][NB];
+#pragma unroll
+    for (int f = 0; f < PF_FRAGS; ++f)
+#pragma unroll
+        for (int t = 0; t < NB; ++t) acc[f][t] = pf_floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    // products of chunk `ch` held in (xb, kb)
+    auto compute = [&](int64_t ch, const uint8_t* xb, const uint8_t* kb) {
+        const uint8_t* cw = kb + wave * PF_FRAGS * PF_CHUNK_GROUPS * TILE_ROWS + lane;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            // one 32-input step at a time: keeps the compiler from hoisting the next step's operand reads
+            // (and their registers) above this step's products
+            __builtin_amdgcn_sched_barrier(0);
+            // this lane's group exists and belongs to this split (not the trailing padding chunk)
+            const bool valid = ch < c1 && ch * PF_CHUNK_GROUPS + 4 * s + kq < p.G;
+            pf_half8_t a[PF_FRAGS];
+#pragma unroll
+            for (int f = 0; f < PF_FRAGS; ++f) {
+                uint32_t w[4];
+#pragma unroll
+                for (int m = 0; m < K; ++m) {
+                    // row r, group 4s + kq of fragment f: byte (4s + kq) * 16 + r = 64 s + lane of its tile
+                    const uint32_t code = cw[(m * PF_TILES + f) * PF_CHUNK_GROUPS * TILE_ROWS + 64 * s];
+                    const uint4 c = cb_lds[m * CODEWORDS + code];
+                    if (m == 0) {
+                        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+                    } else {
+                        w[0] = pf_u32(pf_h2(w[0]) + pf_h2(c.x));
+                        w[1] = pf_u32(pf_h2(w[1]) + pf_h2(c.y));
+                        w[2] = pf_u32(pf_h2(w[2]) + pf_h2(c.z));
+                        w[3] = pf_u32(pf_h2(w[3]) + pf_h2(c.w));
+                    }
+                }
+                const uint4 wv = valid ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0u, 0u, 0u, 0u);
+                a[f] = __builtin_bit_cast(pf_half8_t, wv);
+            }
+#pragma unroll
+            for (int t = 0; t < NB; ++t) {
+                const uint4 bx = *reinterpret_cast<const uint4*>(xb + pf_xslot(t * 16 + r, 4 * s + kq));
+                const pf_half8_t b = __builtin_bit_cast(pf_half8_t, bx);
+#pragma unroll
+                for (int f = 0; f < PF_FRAGS; ++f)
+                    acc[f][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[f], b, acc[f][t], 0, 0, 0);
+            }
+        }
+    };
+
+    // Two chunks per trip: even chunks (relative to c0) live in (x0, k0), odd ones in (x1, k1), so each half
+    // reads one pair of buffers while the next chunk is copied into the other.  An odd count gets one
+    // trailing chunk past the input (zero activations, zero weights, clamped code addresses).  Every
+    // launched split holds at least one chunk (the plan never makes an empty one).
+    const int64_t c1e = c0 + ((c1 - c0 + 1) & ~(int64_t)1);
+    stage(c0, x0, k0);
+    int64_t ch = c0;
+    do {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // this thread's copies of chunk ch have landed
+        __syncthreads();                                     // ... and every thread's; (x1, k1) is free
+        stage(ch + 1, x1, k1);                               // the next chunk's copies overlap these products
+        compute(ch, x0, k0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();                                     // (x0, k0) is free
+        if (ch + 2 < c1e) stage(ch + 2, x0, k0);
+        compute(ch + 1, x1, k1);
+        ch += 2;
+    } while (ch < c1e);
+
+    const int64_t rt0 = rtb + wave * PF_FRAGS;                             // first row tile of this wave
+    // lane l holds rows 4*kq .. 4*kq+3 of each fragment, column t*16 + r
+#pragma unroll
+    for (int f = 0; f < PF_FRAGS; ++f) {
+        const int64_t row0 = (rt0 + f) * TILE_ROWS + 4 * kq;
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+            const int col = col0 + t * 16 + r;
+            if (col >= p.batch) continue;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = row0 + q;
+                if (i >= p.d_out) continue;
+                if (p.direct) p.out[(int64_t)col * p.d_out + i] = h2f(p.scales[i]) * acc[f][t][q];
+                else p.out[((int64_t)blockIdx.z * p.batch + col) * p.d_out + i] = acc[f][t][q];
+            }
+        }
+    }
+}
+
+// B fragments per wave: 128 batch columns per workgroup.  (Wider tiles need more
+// than the 256 accumulator registers a wave has once the loop carries two chunks.)
+constexpr int PF_NB = 8;
+
+struct PfPlan {
+    int64_t n_chunks, row_blocks, col_blocks;
+    int splits, chunks_per_split;
+};
+
+// Splits of the input dimension: the smallest split count that minimises
+// (rounds of workgroups over the 256 compute units) x (chunks per split), one
+// workgroup per compute unit; at most PF_MAX_SPLITS.
+static PfPlan pf_plan(const Geometry& g, int batch) {
+    PfPlan p;
+    p.n_chunks = (g.d_in + PF_CHUNK - 1) / PF_CHUNK;
+    p.row_blocks = (g.n_rt + PF_TILES - 1) / PF_TILES;
+    p.col_blocks = (batch + PF_NB * 16 - 1) / (PF_NB * 16);
+    p.splits = 1;
+    p.chunks_per_split = (int)p.n_chunks;
+    const int64_t tiles = p.row_blocks * p.col_blocks;
+    if (tiles == 0 || p.n_chunks == 0) return p;
+    int64_t best = -1;
+    for (int64_t sp = 1; sp <= PF_MAX_SPLITS && sp <= p.n_chunks; ++sp) {
+        const int64_t cps = (p.n_chunks + sp - 1) / sp;
+        const int64_t used = (p.n_chunks + cps - 1) / cps;
+        const int64_t cost = ((tiles * used + 255) / 256) * cps;
+        if (best < 0 || cost < best) {
+            best = cost;
+            p.splits = (int)used;
+            p.chunks_per_split = (int)cps;
+        }
+    }
+    return p;
+}
+
+size_t gemm_pf_workspace_bytes(const Geometry& g, int batch) {
+    const PfPlan p = pf_plan(g, batch);
+    return p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4 : 0;
+}
+
+template <int K, int NB>
+static hipError_t launch_pf(const PfArgs& a, const PfPlan& pl, hipStream_t s) {
+    hipLaunchKernelGGL((gemm_pf_kernel<K, NB>),
+                       dim3((unsigned)pl.row_blocks, (unsigned)pl.col_blocks, (unsigned)pl.splits),
+                       dim3(64 * PF_WAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int NB>
+static hipError_t launch_pf_k(int k, const PfArgs& a, const PfPlan& pl, hipStream_t s) {
+    switch (k) {
+        case 1: return launch_pf<1, NB>(a, pl, s);
+        case 2: return launch_pf<2, NB>(a, pl, s);
+        case 3: return launch_pf<3, NB>(a, pl, s);
+        case 4: return launch_pf<4, NB>(a, pl, s);
+        case 5: return launch_pf<5, NB>(a, pl, s);
+        case 6: return launch_pf<6, NB>(a, pl, s);
+        case 7: return launch_pf<7, NB>(a, pl, s);
+        default: return launch_pf<8, NB>(a, pl, s);
+    }
+}
+
+hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                          const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
+    const PfPlan pl = pf_plan(g, batch);
+    if (pl.n_chunks == 0) return launch_zero_f32(y, (int64_t)batch * g.d_out, s);   // empty input: Y = 0
+    PfArgs a;
+    a.packed = packed;
+    a.codebooks = reinterpret_cast<const uint4*>(codebooks);
+    a.scales = scales;
+    a.x = x;
+    a.direct = pl.splits == 1 ? 1 : 0;
+    a.out = a.direct ? y : static_cast<float*>(ws);
+    a.d_out = g.d_out;
+    a.d_in = g.d_in;
+    a.G = g.G;
+    a.n_rt = g.n_rt;
+    a.plane_bytes = g.plane_bytes;
+    a.n_chunks = pl.n_chunks;
+    a.batch = batch;
+    a.chunks_per_split = pl.chunks_per_split;
+    const hipError_t e = launch_pf_k<PF_NB>(k, a, pl, s);
+    if (e != hipSuccess || a.direct) return e;
+    return launch_split_reduce(static_cast<const float*>(ws), scales, y, g.d_out, batch, pl.splits, s);
+}
+
+}  // namespace aqd

@@ -283,6 +283,21 @@ __global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
         y[e] = 0.f;
 }
 
+hipError_t launch_split_reduce(const float* part, const uint16_t* scales, float* y, int64_t d_out, int batch,
+                               int splits, hipStream_t s) {
+    if (splits > SB_MAX_SPLITS) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
+                       part, scales, y, d_out, batch, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero_f32(float* y, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sb_zero_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256),
+                       0, s, y, n);
+    return hipGetLastError();
+}
+
 template <int MODE>
 constexpr size_t sb_lds_bytes(int k, int nt) {
     return (size_t)k * CODEWORDS * 16 + 2 * (size_t)XPlanes<MODE>::n * nt * 16 * SB_XROW;
@@ -352,11 +367,7 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                            const SbPlaneCols& pc) {
     const SbPlan p = sb_plan(g, sb_per_cu<MODE>(K, batch));
     const int64_t n = (int64_t)batch * g.d_out;
-    if (p.n_chunks == 0) {                                   // empty input: Y = 0
-        hipLaunchKernelGGL(sb_zero_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
-                           dim3(256), 0, s, y, n);
-        return hipGetLastError();
-    }
+    if (p.n_chunks == 0) return launch_zero_f32(y, n, s);   // empty input: Y = 0
     const bool direct = p.splits == 1;
     constexpr size_t lds = sb_lds_bytes<MODE>(K, NT);
     static const hipError_t attr = hipFuncSetAttribute(
@@ -369,9 +380,7 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                        p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((g.d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
-                       static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits);
-    return hipGetLastError();
+    return launch_split_reduce(static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits, s);
 }
 
 template <int MODE, int K>

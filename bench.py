@@ -351,6 +351,50 @@ def measure_small_batch(aqd, wl, torch, dev, copies: int = 32, reps: int = 2):
     return res
 
 
+def measure_prefill(aqd, wl, torch, dev, reps: int = 5):
+    """Prefill (batch 128 / 512 / 2048 prompt tokens) through the fused dequantize + matrix-core kernel on
+    the 4096x14336 and 14336x4096 shapes, k = 2 and 4.  Beside each, the dense fp16 GEMM of the same shape
+    through torch.matmul (the vendor GEMM library) on an uncompressed weight, as a reference point for what
+    the matrix cores deliver on a plain GEMM here.  At these sizes the work is compute-bound, so no cold
+    copies are needed."""
+    res = []
+    M = 4
+    for d_out, d_in in ((4096, 14336), (14336, 4096)):
+        g = wl.rng(0x9F, extra=d_out)
+        packed = aqd.aqd_pack_codes(torch.from_numpy(wl.gen_codes(g, d_out, d_in, M)).to(dev))
+        cbd = torch.from_numpy(wl.gen_codebooks(g, M)).to(dev)
+        sd = torch.from_numpy(wl.gen_scales(g, d_out)).to(dev)
+        W = torch.randn((d_out, d_in), device=dev, dtype=torch.float32).to(torch.float16)
+        for B in (128, 512, 2048):
+            x = torch.randn((B, d_in), device=dev, dtype=torch.float32).to(torch.float16)
+            y = torch.empty((B, d_out), dtype=torch.float32, device=dev)
+            need = aqd.aqd_gemm_prefill_workspace_bytes(d_out, d_in, M, B)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+            def timed(fn):
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(reps):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) * 1e3 / reps
+            us_dense = timed(lambda: torch.matmul(x, W.t()))
+            flops = 2.0 * B * d_out * d_in
+            for k in (2, 4):
+                us = timed(lambda: aqd.aqd_gemm_prefill(packed, cbd, sd, k, x, d_out, d_in, M, out=y, workspace=ws))
+                res.append({"shape": [d_out, d_in], "k": k, "batch": B, "us": us, "tokens_per_s": B * 1e6 / us,
+                            "tflops": flops / us / 1e6, "frac_mfma_peak": flops / us / 1e6 / 2500.0,
+                            "dense_fp16_gemm_us": us_dense, "dense_fp16_gemm_tflops": flops / us_dense / 1e6})
+            del x, y, ws
+        del packed, W
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -362,6 +406,7 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 32-layer decoder-stack measurement")
     ap.add_argument("--no-small-batch", action="store_true", help="skip the small-batch matrix-core measurement")
     ap.add_argument("--no-batched", action="store_true", help="skip the batch 2/4/8 GEMV measurement")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (batch 128..2048) measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 64 MiB device copy first (scale reference for memory counters)")
     args = ap.parse_args()
@@ -478,6 +523,7 @@ def main():
     stack = None if args.no_stack else measure_stack(aqd, wl, torch, dev)
     small = None if args.no_small_batch else measure_small_batch(aqd, wl, torch, dev)
     tiered = None if args.no_small_batch else measure_tiered(aqd, wl, torch, dev)
+    prefill = None if args.no_prefill else measure_prefill(aqd, wl, torch, dev)
 
     value = float(np.mean([per_k[k]["us_per_gemv"] for k in KS]))
     k4 = per_k[4]
@@ -522,6 +568,8 @@ def main():
         result["small_batch"] = small
     if tiered is not None:
         result["tiered_batch"] = tiered
+    if prefill is not None:
+        result["prefill"] = prefill
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, cb, s, x, args.cpu_budget, y_check)
     print(json.dumps(result))

@@ -285,6 +285,42 @@ aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* cod
                                 float* y, int32_t batch, const aqd_layer* layer,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Prefill / large-batch product on the matrix cores, batch 1..32768.  The
+ * compute-bound regime of the same linear (Drop-by-Drop, section 3.2: each
+ * weight group is the sum of its codewords; section 5: the first k
+ * codebooks).  The ApexQuant page, appendix H "Nested decoding in service",
+ * notes that prefill is compute-bound and leaves it unmeasured:
+ *
+ *     y[n][i] = s_i * sum_c W_k[i][c] * x_rot[n][c]      (fp32 out)
+ *
+ * Each workgroup rebuilds 256 weight rows as fp16 codeword sums (packed fp16
+ * adds, as the fp16 small-batch mode) and multiplies them by 128 activation
+ * columns with v_mfma_f32_16x16x32_f16, accumulating in fp32.  Throughput is
+ * meant for batch >= 128; any batch in range is correct.
+ *
+ * packed_codes, codebooks, scales: as for aqd_gemv; only the first k planes
+ *               and codebooks are read.
+ * x_rot:        fp16 [batch][d_in], the rotated activation, 16-byte aligned.
+ * y:            fp32 [batch][d_out], 4-byte aligned.
+ * k:            1..M.  batch: 1..AQD_PREFILL_MAX_BATCH.
+ * workspace:    aqd_gemm_prefill_workspace_bytes(layer, batch) bytes (0 when
+ *               the tiles fill the chip without splitting the inputs; NULL is
+ *               then allowed), 16-byte aligned, fully overwritten by every
+ *               call; calls that may overlap in time need separate ones.
+ * The summation order is fixed (input splits are added in order by a second
+ * kernel), so repeating a call gives the same bits.
+ * Errors: AQD_ERR_SHAPE for batch out of range, otherwise as for
+ * aqd_gemm_small_batch.
+ * ------------------------------------------------------------------------- */
+#define AQD_PREFILL_MAX_BATCH 32768
+
+size_t aqd_gemm_prefill_workspace_bytes(const aqd_layer* layer, int32_t batch);
+
+aqd_status aqd_gemm_prefill(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales,
+                            int32_t k, const uint16_t* x_rot, float* y, int32_t batch, const aqd_layer* layer,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

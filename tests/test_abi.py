@@ -224,3 +224,25 @@ def test_grouped_gemv_rejects_bad_arguments(L):
     assert L.aqd_rotate_gemv_grouped_signed(lins(5), 5, 1, FAKE, 256, 64, sg, FAKE, 1 << 20, None) == E_SHAPE
     assert L.aqd_rotate_gemv_grouped_signed(big, 3, 2, FAKE, 4096, 128, sg, None, 0, None) == E_WS
     assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 3, FAKE, 256, 64, sg, FAKE, 1 << 20, None) == E_K
+
+
+def test_prefill_rejects_bad_arguments(L):
+    def pf(packed=FAKE, cb=FAKE, s=FAKE, k=1, x=FAKE, y=FAKE, batch=256, layer=None, ws=FAKE, nws=1 << 30):
+        return L.aqd_gemm_prefill(packed, cb, s, k, x, y, batch, layer if layer is not None else lay(), ws, nws,
+                                  None)
+    assert pf(batch=0) == E_SHAPE
+    assert pf(batch=aqd.AQD_PREFILL_MAX_BATCH + 1) == E_SHAPE
+    assert pf(k=3) == E_K                         # M = 2
+    assert pf(k=0) == E_K
+    assert pf(x=None) == E_NULL
+    assert pf(y=FAKE + 2) == E_ALIGN               # fp32 output
+    assert pf(x=FAKE_ODD) == E_ALIGN
+    assert pf(layer=lay(d_in=100)) == E_SHAPE
+    assert pf(layer=lay(d_out=0), y=None) == OK   # nothing to compute
+    big = lay(d_out=4096, d_in=14336, M=4)
+    need = L.aqd_gemm_prefill_workspace_bytes(big, 512)
+    assert need > 0                                # 16 row blocks x 4 column blocks: the inputs are split
+    assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, None, 0, None) == E_WS
+    assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, FAKE, need - 1, None) == E_WS
+    assert L.aqd_gemm_prefill_workspace_bytes(lay(d_out=14336, d_in=4096, M=4), 4096) == 0   # no split
+    assert L.aqd_gemm_prefill_workspace_bytes(big, 0) == 0

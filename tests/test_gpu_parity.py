@@ -504,14 +504,14 @@ def test_rotate_gemv_grouped_signed(orc, shapes, d_in, block, k):
 
 
 def test_quantized_linear_signed(orc):
-    """A layer with a sign mask: batch 1 (one launch), batch 4 (GEMV) and batch 16 (matrix cores)."""
+    """A layer with a sign mask: batch 1 (one launch), 4 (GEMV), 16 (small batch) and 130 (prefill)."""
     g = wl.rng(99)
     d_out, d_in, M, block, k = 512, 1024, 4, 128, 3
     codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
     signs = wl.gen_signs(g, d_in)
     cdev, cbdev, sdev = _layer_dev(codes, cb, s)
     ql = aqd.QuantizedLinear(cdev, cbdev, sdev, block, signs=to_dev(signs))
-    for batch in (1, 4, 16):
+    for batch in (1, 4, 16, 130):
         x = wl.gen_x(g, batch, d_in, "f16")
         y = ql.forward(to_dev(x), k).float().cpu().numpy()
         ref = orc.linear(codes, cb, s, k, orc.rotate_signed(x, signs, block))
@@ -567,3 +567,74 @@ def test_small_batch_tiered_edge(orc):
     for n, k in enumerate(ks):
         assert np.array_equal(y[n].astype(np.float64), orc.linear(codes, cb, s, k, xq[n:n + 1])[0]), n
 
+
+# ---------------------------------------------------------------------------
+# prefill / large batch on the matrix cores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,M,batches", [
+    (1000, 1000, 3, (1, 130, 200)),   # ragged rows, a ragged 64-input chunk, columns past one 128-column tile
+    (17, 64, 2, (1, 5, 129)),         # one chunk, rows inside one fragment
+    (512, 960, 4, (128,)),            # 15 chunks split one per workgroup: odd chunk counts per split
+    (33, 8, 8, (3,)),                 # one group, M = 8, every k
+])
+def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
+    g = wl.rng(51, extra=d_out * 7 + d_in + M)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    xr = wl.gen_x(g, max(batches), d_in, "f16")          # stands for an already rotated activation
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    for k in range(1, M + 1):
+        ref = orc.linear(codes, cb, s, k, xr)
+        for B in batches:
+            y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(xr[:B]), d_out, d_in, M).cpu().numpy()
+            e = normwise(y, ref[:B])
+            record(test="prefill_edge", shape=[d_out, d_in, M], k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
+
+
+def test_prefill_dyadic_bit_exact(orc):
+    """Exact arithmetic: every split, chunk and column of the tiled product gives the oracle's bits."""
+    d_out, d_in, M = 300, 2048, 4
+    codes, cb, s, x = wl.dyadic_case(wl.rng(52), d_out, d_in, M, batch=160)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    for k in (1, 4):
+        ref = orc.linear(codes, cb, s, k, x)
+        y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(x), d_out, d_in, M).cpu().numpy()
+        assert np.array_equal(y.astype(np.float64), ref), k
+
+
+@pytest.mark.parametrize("d_out,d_in,batch,k", [
+    (4096, 14336, 512, 4),      # down projection, 512 prompt tokens
+    (4096, 14336, 512, 2),
+    (14336, 4096, 1024, 4),     # gate / up projection, 1024 prompt tokens
+])
+def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
+    """Full 8B-shape layers in the launch configuration the benchmark times; eight sampled columns
+    against the oracle, and a repeated call gives the same bits."""
+    M = 4
+    g = wl.rng(53, extra=d_out + batch + k)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    x = wl.gen_x(g, batch, d_in, "f16")
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xd = to_dev(x)
+    y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, xd, d_out, d_in, M)
+    y2 = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, xd, d_out, d_in, M)
+    assert torch.equal(y, y2)
+    cols = np.sort(np.random.Generator(np.random.PCG64(54)).choice(batch, size=8, replace=False))
+    ref = orc.linear(codes, cb, s, k, x[cols])
+    e = normwise(y.cpu().numpy()[cols], ref)
+    record(test="prefill_full", shape=[d_out, d_in], batch=batch, k=k, err=e)
+    assert e <= TOL, e
+
+
+def test_prefill_empty_input_gives_zero():
+    d_out = 40
+    s = to_dev(np.ones(d_out, dtype=np.float16))
+    y = torch.full((130, d_out), 7.0, dtype=torch.float32, device=dev())
+    aqd.aqd_gemm_prefill(torch.empty(0, dtype=torch.uint8, device=dev()),
+                         torch.empty(0, dtype=torch.float16, device=dev()), s, 1,
+                         torch.empty((130, 0), dtype=torch.float16, device=dev()), d_out, 0, 2, out=y)
+    assert torch.count_nonzero(y).item() == 0
