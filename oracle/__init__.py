@@ -76,6 +76,7 @@ class Oracle:
         lib.oracle_bits_per_param.restype = ctypes.c_double
         lib.oracle_bits_per_param.argtypes = [_i64, _i64, _i32, _i32, _i32]
         lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_encode_greedy.argtypes = [ctypes.POINTER(ctypes.c_float), _c_u16p, _i64, _i64, _i32, _c_u8p]
 
     # -- number formats --------------------------------------------------
     def decode(self, a: np.ndarray, dtype: str = "f16") -> np.ndarray:
@@ -207,6 +208,21 @@ class Oracle:
         out = np.empty((d_out, G, M), dtype=np.uint8)
         assert self.lib.oracle_unpack_codes(_ptr(packed, _c_u8p), d_out, G, M, _ptr(out, _c_u8p)) == 0
         return out
+
+    # -- encode ----------------------------------------------------------
+    def encode_greedy(self, target: np.ndarray, codebooks: np.ndarray, M: Optional[int] = None) -> np.ndarray:
+        """Greedy residual codes [d_out][G][M] (uint8) for float32 targets [d_out][d_in] (rotated weights
+        divided by their row scale) and fp16 codebooks [M][256][8]."""
+        t = np.ascontiguousarray(target, dtype=np.float32)
+        cb = np.ascontiguousarray(codebooks).view(np.uint16)
+        M = cb.shape[0] if M is None else M
+        d_out, d_in = t.shape
+        codes = np.empty((d_out, d_in // 8, M), dtype=np.uint8)
+        rc = self.lib.oracle_encode_greedy(t.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(cb, _c_u16p),
+                                           d_out, d_in, M, _ptr(codes, _c_u8p))
+        if rc != 0:
+            raise ValueError(f"oracle_encode_greedy rc={rc}")
+        return codes
 
     # -- storage ---------------------------------------------------------
     def storage_bits(self, d_out: int, d_in: int, g: int, M: int, B: int) -> float:

@@ -465,6 +465,66 @@ double oracle_bits_per_param(int64_t d_out, int64_t d_in, int32_t g, int32_t M, 
 }
 
 /* ---------------------------------------------------------------------------
+ * Encode side: greedy residual code assignment for fixed codebooks.
+ *
+ * Section 3.2 defines the decoder (a group is the sum of one codeword from
+ * each codebook) and section 5 the prefix order (codebook 1 first).  The
+ * pages do not include AQLM's search for the codes (its appendix is not on
+ * them), so this is a stated stand-in that respects the prefix order: for
+ * every group of 8 target values, codebook m = 0, 1, ..., M-1 in turn picks
+ * the codeword nearest (squared Euclidean distance) to the residual that the
+ * earlier codebooks left, and the residual loses that codeword.
+ *
+ * The target is the weight group already rotated and divided by its row
+ * scale.  The pages fix no precision for this search; the decision is an
+ * index, so it is taken in float32 with one fixed operation order, which the
+ * GPU encoder follows too:
+ *     e_t = r_t - C[c][t]  (float),  d = fmaf(e_t, e_t, d) for t = 0..7 from d = 0,
+ * the smallest d wins and equal d go to the lower index; then r_t = r_t - C[c*][t].
+ * codebooks are the fp16 codebooks decoded exactly; codes: [d_out][G][M].
+ * ------------------------------------------------------------------------- */
+int oracle_encode_greedy(const float *target, const uint16_t *codebooks, int64_t d_out, int64_t d_in, int32_t M,
+                         uint8_t *codes)
+{
+    if (d_out < 0 || d_in < 0 || d_in % ORACLE_GROUP != 0 || M < 1)
+        return -1;
+    const int64_t G = d_in / ORACLE_GROUP;
+    float *cbf = (float *)malloc(sizeof(float) * (size_t)M * ORACLE_CODEWORDS * ORACLE_GROUP);
+    if (!cbf)
+        return -2;
+    for (int64_t e = 0; e < (int64_t)M * ORACLE_CODEWORDS * ORACLE_GROUP; ++e)
+        cbf[e] = (float)oracle_f16_to_f64(codebooks[e]);
+    int64_t q;
+#pragma omp parallel for schedule(static)
+    for (q = 0; q < d_out * G; ++q) {
+        float r[ORACLE_GROUP];
+        for (int t = 0; t < ORACLE_GROUP; ++t)
+            r[t] = target[q * ORACLE_GROUP + t];
+        for (int32_t m = 0; m < M; ++m) {
+            const float *cm = cbf + (int64_t)m * ORACLE_CODEWORDS * ORACLE_GROUP;
+            int best = 0;
+            float best_d = 0.0f;
+            for (int c = 0; c < ORACLE_CODEWORDS; ++c) {
+                float d = 0.0f;
+                for (int t = 0; t < ORACLE_GROUP; ++t) {
+                    const float e = r[t] - cm[c * ORACLE_GROUP + t];
+                    d = fmaf(e, e, d);
+                }
+                if (c == 0 || d < best_d) {
+                    best = c;
+                    best_d = d;
+                }
+            }
+            codes[q * M + m] = (uint8_t)best;
+            for (int t = 0; t < ORACLE_GROUP; ++t)
+                r[t] = r[t] - cm[best * ORACLE_GROUP + t];
+        }
+    }
+    free(cbf);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Threading control for the timing leg and the determinism pin.
  * ------------------------------------------------------------------------- */
 

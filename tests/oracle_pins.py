@@ -411,6 +411,67 @@ def pin_storage_worked_example(orc):
         assert M < orc.bits_per_param(4096, 14336, 8, M, 8) < M + 0.01
 
 
+# ---------------------------------------------------------------------------
+# encode side: greedy residual code assignment
+# ---------------------------------------------------------------------------
+
+def _sign_codebooks(M: int) -> np.ndarray:
+    """Codebook m holds every +-8^-m sign pattern: codeword c has +8^-m at element t where bit t of c is
+    set, -8^-m elsewhere (fp16-exact)."""
+    bits = (np.arange(256)[:, None] >> np.arange(8)[None, :]) & 1
+    pat = np.where(bits == 1, 1.0, -1.0)
+    return np.stack([pat * 8.0 ** -m for m in range(M)]).astype(np.float16)
+
+
+def pin_encode_planted_codes(orc):
+    """Targets that are exact sums of one +-1, one +-1/8, one +-1/64 and one +-1/512 sign pattern: at each
+    stage the remaining scales add up to less than the gap to a wrong sign, so the greedy search must
+    return exactly the planted codes, plane by plane."""
+    g = _rng(20)
+    M, d_out, G = 4, 5, 12
+    cb = _sign_codebooks(M)
+    planted = g.integers(0, 256, size=(d_out, G, M))
+    target = np.zeros((d_out, G, 8))
+    for m in range(M):
+        target += cb[m].astype(np.float64)[planted[:, :, m]]
+    codes = orc.encode_greedy(target.reshape(d_out, G * 8).astype(np.float32), cb)
+    assert np.array_equal(codes, planted.astype(np.uint8))
+    # a prefix of the planes only: the first two planes come out the same
+    assert np.array_equal(orc.encode_greedy(target.reshape(d_out, G * 8).astype(np.float32), cb[:2]),
+                          planted[:, :, :2].astype(np.uint8))
+
+
+def pin_encode_is_stagewise_nearest(orc):
+    """Gaussian targets, N(0, 0.05) codebooks: every stage picks a nearest codeword to the residual left by
+    the earlier stages (checked in float64 against all 256; float32 rounding may only break near-ties)."""
+    g = _rng(21)
+    M, d_out, d_in = 3, 7, 96
+    cb = wl.gen_codebooks(g, M)
+    target = (g.standard_normal((d_out, d_in)) * 0.1).astype(np.float32)
+    codes = orc.encode_greedy(target, cb)
+    C = cb.astype(np.float64)
+    r = target.astype(np.float64).reshape(d_out, d_in // 8, 8)
+    for m in range(M):
+        d = ((r[:, :, None, :] - C[m][None, None, :, :]) ** 2).sum(-1)        # [d_out][G][256]
+        chosen = np.take_along_axis(d, codes[:, :, m][:, :, None].astype(np.int64), axis=2)[..., 0]
+        assert np.all(chosen <= d.min(axis=2) * (1 + 1e-5) + 1e-12), m
+        r = r - C[m][codes[:, :, m]]
+
+
+def pin_encode_ties_go_to_lower_index(orc):
+    """Equal codewords: the lower index wins.  A target equal to a codeword leaves a zero residual, after
+    which the next plane picks its shortest codeword (the first one among equals)."""
+    g = _rng(22)
+    cb = (g.standard_normal((2, 256, 8)) * 0.05).astype(np.float16)
+    cb[0, 9] = cb[0, 5]
+    cb[0, 200] = cb[0, 5]
+    cb[1, 77] = 0.0
+    cb[1, 140] = 0.0
+    target = cb[0, 5].astype(np.float32)[None, :]
+    codes = orc.encode_greedy(target, cb)
+    assert codes[0, 0, 0] == 5 and codes[0, 0, 1] == 77, codes
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -28,10 +28,18 @@ MUTANTS = {
     "sign_bits_msb_first": ("eps[c] = ((signs[c / 8] >> (c % 8)) & 1u)", "eps[c] = ((signs[c / 8] >> (7 - c % 8)) & 1u)"),
     "sign_block_offset_dropped": ("const double *es = eps + beta * b;", "const double *es = eps;"),
     "signed_no_normalisation": ("os[r] = acc * inv;", "os[r] = acc;"),
+    "encode_residual_not_updated": ("r[t] = r[t] - cm[best * ORACLE_GROUP + t];", "r[t] = r[t];"),
+    "encode_ties_to_higher_index": ("if (c == 0 || d < best_d) {", "if (c == 0 || d <= best_d) {"),
+    "encode_one_plane_for_all": ("const float *cm = cbf + (int64_t)m * ORACLE_CODEWORDS * ORACLE_GROUP;",
+                                 "const float *cm = cbf;"),
+    "encode_elements_reversed": ("const float e = r[t] - cm[c * ORACLE_GROUP + t];",
+                                 "const float e = r[t] - cm[c * ORACLE_GROUP + (ORACLE_GROUP - 1 - t)];"),
+    "encode_planes_stored_reversed": ("codes[q * M + m] = (uint8_t)best;", "codes[q * M + (M - 1 - m)] = (uint8_t)best;"),
     "first_codebook_dropped": ("for (int32_t m = 0; m < k; ++m) {", "for (int32_t m = 1; m < k; ++m) {"),
     "prefix_ignored": ("for (int32_t m = 0; m < k; ++m) {", "for (int32_t m = 0; m < M; ++m) {"),
     "planes_reversed": ("const uint8_t c = codes[(i * G + j) * M + m];", "const uint8_t c = codes[(i * G + j) * M + (M - 1 - m)];"),
-    "codeword_elements_reversed": ("* ORACLE_GROUP + t];", "* ORACLE_GROUP + (ORACLE_GROUP - 1 - t)];"),
+    "codeword_elements_reversed": ("g += codebooks[((int64_t)m * ORACLE_CODEWORDS + c) * ORACLE_GROUP + t];",
+                                   "g += codebooks[((int64_t)m * ORACLE_CODEWORDS + c) * ORACLE_GROUP + (ORACLE_GROUP - 1 - t)];"),
     "scale_dropped": ("const double s = scales ? scales[i] : 1.0;", "const double s = 1.0;"),
     "groups_transposed": ("w[j * ORACLE_GROUP + t] = s * g;", "w[t * G + j] = s * g;"),
     "matvec_index_reversed": ("acc += w[c] * xr[c];", "acc += w[c] * xr[d_in - 1 - c];"),
