@@ -62,6 +62,7 @@ _SIGNATURES = {
     "aqd_rotate_gemv_grouped": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _SZ, _VP]),
     "aqd_gemm_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(aqd_layer), _I32]),
     "aqd_gemm_prefill": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, ctypes.POINTER(aqd_layer), _VP, _SZ, _VP]),
+    "aqd_encode_greedy": (_INT, [_VP, _VP, _I32, _I64, _I64, _VP, _VP]),
     "aqd_rotate_gemv_grouped_signed": (_INT, [ctypes.POINTER(aqd_linear), _I32, _I32, _VP, _I64, _I32, _VP, _VP,
                                               _SZ, _VP]),
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
@@ -267,6 +268,18 @@ def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: 
     _check(lib().aqd_gemm_small_batch(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x_rot), x_dtype,
                                       _ptr(out), batch, ctypes.byref(L), _ptr(workspace),
                                       workspace.numel() if workspace is not None else 0, _stream()))
+    return out
+
+
+def aqd_encode_greedy(target: torch.Tensor, codebooks: torch.Tensor, M: Optional[int] = None,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Greedy residual codes uint8 [d_out][d_in/8][M] for float32 targets [d_out][d_in] (rotated weights
+    divided by their row scale) and fp16 codebooks [M][256][8]."""
+    d_out, d_in = target.shape
+    M = codebooks.shape[0] if M is None else M
+    if out is None:
+        out = torch.empty((d_out, d_in // 8, M), dtype=torch.uint8, device=target.device)
+    _check(lib().aqd_encode_greedy(_ptr(target), _ptr(codebooks), M, d_out, d_in, _ptr(out), _stream()))
     return out
 
 

@@ -91,6 +91,10 @@ size_t gemm_pf_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s);
 
+// encode side: greedy residual codes [d_out][d_in/8][M] for fp32 targets [d_out][d_in]
+hipError_t launch_encode_greedy(const float* target, const uint16_t* codebooks, int M, int64_t d_out,
+                                int64_t d_in, uint8_t* codes, hipStream_t s);
+
 // ---- device helpers --------------------------------------------------------
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 

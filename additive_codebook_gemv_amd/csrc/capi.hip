@@ -319,4 +319,18 @@ aqd_status aqd_gemm_prefill(const uint8_t* packed_codes, const uint16_t* codeboo
                       "aqd_gemm_prefill");
 }
 
+aqd_status aqd_encode_greedy(const float* target, const uint16_t* codebooks, int32_t M, int64_t d_out,
+                             int64_t d_in, uint8_t* codes, void* stream) {
+    if (M < 1 || M > MAX_M) return fail(AQD_ERR_SHAPE, "M must be in [1, 8]");
+    if (d_out < 0 || d_out > MAX_DIM || d_in < 0 || d_in > MAX_DIM) return fail(AQD_ERR_SHAPE, "d_out or d_in out of range");
+    if (d_in % 8) return fail(AQD_ERR_SHAPE, "d_in must be a multiple of 8");
+    if (d_out * d_in == 0) return AQD_OK;
+    if ((d_out * (d_in / 8) + 255) / 256 > 0x7FFFFFFF) return fail(AQD_ERR_SHAPE, "too many groups for one launch");
+    if (!target || !codebooks || !codes) return fail(AQD_ERR_NULL, "target, codebooks or codes is NULL");
+    if (!aligned16(target)) return fail(AQD_ERR_ALIGN, "target must be 16-byte aligned");
+    if (!aligned2(codebooks)) return fail(AQD_ERR_ALIGN, "codebooks must be 2-byte aligned");
+    return hip_status(launch_encode_greedy(target, codebooks, M, d_out, d_in, codes, (hipStream_t)stream),
+                      "aqd_encode_greedy");
+}
+
 }  // extern "C"

@@ -351,6 +351,50 @@ def measure_small_batch(aqd, wl, torch, dev, copies: int = 32, reps: int = 2):
     return res
 
 
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+
+
+def measure_encode(aqd, wl, torch, dev, reps: int = 3):
+    """Greedy residual encoding of the 4096x14336 layer (M = 4, N(0, 0.05) codebooks, rotated Gaussian
+    weights and their row scales): time per layer, and the weight error of the encoded layer per k.
+    Work per code group and codebook: 256 squared distances of 8 elements (8 subtractions and 8 fmas,
+    24 flops each) plus the residual update; the kernel is fp32 ALU-bound."""
+    d_out, d_in, M = 4096, 14336, 4
+    g = wl.rng(0xE1)
+    cb = wl.gen_codebooks(g, M)
+    w, s, target = wl.gen_encode_targets(g, d_out, d_in, M)
+    td, cbd = torch.from_numpy(target).to(dev), torch.from_numpy(cb).to(dev)
+    codes = torch.empty((d_out, d_in // 8, M), dtype=torch.uint8, device=dev)
+    aqd.aqd_encode_greedy(td, cbd, out=codes)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        aqd.aqd_encode_greedy(td, cbd, out=codes)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    groups = d_out * (d_in // 8)
+    flops = groups * M * (256 * 24 + 8)
+    # weight error of the encoded layer per k (a diagnostic, computed with torch on the device)
+    wd = torch.from_numpy(w).to(dev)
+    cbf = cbd.float()
+    sd = torch.from_numpy(s).to(dev).float()[:, None]
+    acc = torch.zeros((d_out, d_in // 8, 8), dtype=torch.float32, device=dev)
+    errs = []
+    for m in range(M):
+        acc += cbf[m][codes[:, :, m].long()]
+        errs.append(float(torch.linalg.norm(sd * acc.reshape(d_out, d_in) - wd) / torch.linalg.norm(wd)))
+    del td, codes, wd, acc
+    torch.cuda.empty_cache()
+    return {"workload": "encode 4096x14336 (M = 4, g = 8): rotated N(0,1) weights, fp16 row scales, "
+                        "N(0, 0.05) fp16 codebooks; greedy residual codes",
+            "us": us, "weights_per_s": d_out * d_in * 1e6 / us,
+            "roofline": {"bound": "alu", "achieved": flops / us / 1e6, "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": flops / us / 1e6 / FP32_VECTOR_PEAK_TFLOPS},
+            "rel_weight_error_per_k": errs}
+
+
 def measure_prefill(aqd, wl, torch, dev, reps: int = 5):
     """Prefill (batch 128 / 512 / 2048 prompt tokens) through the fused dequantize + matrix-core kernel on
     the 4096x14336 and 14336x4096 shapes, k = 2 and 4.  Beside each, the dense fp16 GEMM of the same shape
@@ -407,6 +451,7 @@ def main():
     ap.add_argument("--no-small-batch", action="store_true", help="skip the small-batch matrix-core measurement")
     ap.add_argument("--no-batched", action="store_true", help="skip the batch 2/4/8 GEMV measurement")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill (batch 128..2048) measurement")
+    ap.add_argument("--no-encode", action="store_true", help="skip the encoder measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run one plain 64 MiB device copy first (scale reference for memory counters)")
     args = ap.parse_args()
@@ -524,6 +569,7 @@ def main():
     small = None if args.no_small_batch else measure_small_batch(aqd, wl, torch, dev)
     tiered = None if args.no_small_batch else measure_tiered(aqd, wl, torch, dev)
     prefill = None if args.no_prefill else measure_prefill(aqd, wl, torch, dev)
+    encode = None if args.no_encode else measure_encode(aqd, wl, torch, dev)
 
     value = float(np.mean([per_k[k]["us_per_gemv"] for k in KS]))
     k4 = per_k[4]
@@ -570,6 +616,8 @@ def main():
         result["tiered_batch"] = tiered
     if prefill is not None:
         result["prefill"] = prefill
+    if encode is not None:
+        result["encode"] = encode
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(codes, cb, s, x, args.cpu_budget, y_check)
     print(json.dumps(result))

@@ -321,6 +321,33 @@ aqd_status aqd_gemm_prefill(const uint8_t* packed_codes, const uint16_t* codeboo
                             int32_t k, const uint16_t* x_rot, float* y, int32_t batch, const aqd_layer* layer,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Encode side: greedy residual code assignment for fixed codebooks.
+ *
+ * Drop-by-Drop section 3.2 gives the decoder (a group is the sum of one
+ * codeword per codebook) and section 5 the prefix order; AQLM's own code
+ * search is not on the pages.  This stand-in respects the prefix order: for
+ * every group of 8 targets, codebook m = 0, 1, ..., M-1 in turn takes the
+ * codeword nearest (squared Euclidean distance) to the residual the earlier
+ * codebooks left, and the residual loses it, so every prefix of the codes is
+ * the greedy code for that many codebooks.
+ *
+ * The decision is taken in float32 with one fixed operation order:
+ *   e_t = r_t - C[c][t];  d = fma(e_t, e_t, d) for t = 0..7 from d = 0;
+ *   the smallest d wins, equal d go to the lower index;  r_t = r_t - C[c*][t].
+ *
+ * target:    float32 [d_out][d_in], 16-byte aligned: the weights already
+ *            rotated (W Q^T, e.g. aqd_hadamard_rotate of the rows with F32
+ *            in and out) and divided by their row scale.
+ * codebooks: fp16 [M][256][8], 2-byte aligned.  M: 1..8.
+ * codes:     uint8 [d_out][d_in/8][M] out (the logical layout aqd_pack_codes
+ *            takes).  All pointers are device memory owned by the caller.
+ * Errors: AQD_ERR_SHAPE for M outside 1..8, d_in not a multiple of 8 or
+ * sizes out of range; AQD_ERR_NULL / AQD_ERR_ALIGN as usual.
+ * ------------------------------------------------------------------------- */
+aqd_status aqd_encode_greedy(const float* target, const uint16_t* codebooks, int32_t M, int64_t d_out,
+                             int64_t d_in, uint8_t* codes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

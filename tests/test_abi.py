@@ -246,3 +246,17 @@ def test_prefill_rejects_bad_arguments(L):
     assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, FAKE, need - 1, None) == E_WS
     assert L.aqd_gemm_prefill_workspace_bytes(lay(d_out=14336, d_in=4096, M=4), 4096) == 0   # no split
     assert L.aqd_gemm_prefill_workspace_bytes(big, 0) == 0
+
+
+def test_encode_rejects_bad_arguments(L):
+    def enc(t=FAKE, cb=FAKE, M=2, d_out=64, d_in=256, codes=FAKE):
+        return L.aqd_encode_greedy(t, cb, M, d_out, d_in, codes, None)
+    assert enc(M=0) == E_SHAPE
+    assert enc(M=9) == E_SHAPE
+    assert enc(d_in=100) == E_SHAPE
+    assert enc(d_out=-1) == E_SHAPE
+    assert enc(t=None) == E_NULL
+    assert enc(codes=None) == E_NULL
+    assert enc(t=FAKE_ODD) == E_ALIGN              # float4 loads
+    assert enc(cb=FAKE + 1) == E_ALIGN
+    assert enc(d_out=0, t=None) == OK              # nothing to encode

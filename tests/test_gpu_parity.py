@@ -638,3 +638,60 @@ def test_prefill_empty_input_gives_zero():
                          torch.empty(0, dtype=torch.float16, device=dev()), s, 1,
                          torch.empty((130, 0), dtype=torch.float16, device=dev()), d_out, 0, 2, out=y)
     assert torch.count_nonzero(y).item() == 0
+
+
+# ---------------------------------------------------------------------------
+# encode side: greedy residual code assignment
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,M", [(300, 1000, 4), (17, 64, 8), (1, 8, 1), (1000, 512, 2)])
+def test_encode_bit_exact(orc, d_out, d_in, M):
+    """Codes are index work: the GPU encoder returns exactly the oracle's codes (same float32 decision)."""
+    g = wl.rng(61, extra=d_out + d_in + M)
+    cb = wl.gen_codebooks(g, M)
+    _, _, target = wl.gen_encode_targets(g, d_out, d_in, M)
+    got = aqd.aqd_encode_greedy(to_dev(target), to_dev(cb)).cpu().numpy()
+    want = orc.encode_greedy(target, cb)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:5].tolist()}"
+
+
+def test_encode_planted_codes():
+    """Sign-pattern codebooks at scales 1, 1/8, 1/64, 1/512: the planted codes come back exactly."""
+    g = wl.rng(62)
+    M, d_out, G = 4, 64, 40
+    bits = (np.arange(256)[:, None] >> np.arange(8)[None, :]) & 1
+    cb = np.stack([np.where(bits == 1, 1.0, -1.0) * 8.0 ** -m for m in range(M)]).astype(np.float16)
+    planted = g.integers(0, 256, size=(d_out, G, M))
+    target = np.zeros((d_out, G, 8))
+    for m in range(M):
+        target += cb[m].astype(np.float64)[planted[:, :, m]]
+    got = aqd.aqd_encode_greedy(to_dev(target.reshape(d_out, G * 8).astype(np.float32)), to_dev(cb)).cpu().numpy()
+    assert np.array_equal(got, planted.astype(np.uint8))
+
+
+def test_encode_full_size_sampled_and_decoded(orc):
+    """The 4096x14336 layer (M = 4): sampled rows equal the oracle's codes; the encoded layer, packed and
+    run through the GEMV, reproduces the oracle's output for those codes, and the weight error falls with k."""
+    d_out, d_in, M = 4096, 14336, 4
+    g = wl.rng(63)
+    cb = wl.gen_codebooks(g, M)
+    w, s, target = wl.gen_encode_targets(g, d_out, d_in, M)
+    codes = aqd.aqd_encode_greedy(to_dev(target), to_dev(cb))
+    rows = np.sort(np.random.Generator(np.random.PCG64(64)).choice(d_out, size=48, replace=False))
+    want = orc.encode_greedy(target[rows], cb)
+    assert np.array_equal(codes.cpu().numpy()[rows], want)
+    # decode side on the sampled rows: the GEMV of the GPU-encoded layer against the oracle's output for
+    # the oracle's own codes of those rows
+    x = wl.gen_x(g, 1, d_in, "f16")
+    y = aqd.aqd_gemv(aqd.aqd_pack_codes(codes), to_dev(cb), to_dev(s), M, to_dev(x), d_out, d_in, M)
+    ref = orc.linear(want, cb, s[rows], M, x)
+    e = normwise(y.float().cpu().numpy()[:, rows], ref)
+    assert e <= TOL, e
+    # weight error of the encoded rows against the rotated weights, per k: falls with every codebook
+    errs = []
+    for k in range(1, M + 1):
+        wk = orc.reconstruct(want, cb, s[rows], k)
+        errs.append(np.linalg.norm(wk - w[rows].astype(np.float64)) / np.linalg.norm(w[rows]))
+    record(test="encode_error_curve", rel_err=errs)
+    assert all(a > b for a, b in zip(errs, errs[1:])), errs

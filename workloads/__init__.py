@@ -70,6 +70,23 @@ def gen_signs(g: np.random.Generator, d_in: int) -> np.ndarray:
     return g.integers(0, 256, size=d_in // 8, dtype=np.uint8)
 
 
+def gen_encode_targets(g: np.random.Generator, d_out: int, d_in: int, M: int, sigma_c: float = 0.05):
+    """Synthetic encoder input: rotated Gaussian weights and their row scales.
+
+    W Q^T of an i.i.d. Gaussian W under an orthonormal Q is again i.i.d.
+    Gaussian, so the rotated weights are drawn directly as N(0, 1) float32.
+    The row scale is chosen so the scaled row has the RMS of a sum of M
+    codewords with N(0, sigma_c) entries: s_i = fp16(rms_i / (sigma_c sqrt(M))).
+    Returns (w_rot float32 [d_out][d_in], scales fp16 [d_out],
+    target float32 [d_out][d_in] = w_rot / s_i).
+    """
+    w = g.standard_normal((d_out, d_in)).astype(np.float32)
+    rms = np.sqrt(np.mean(w.astype(np.float64) ** 2, axis=1)) if d_in else np.ones(d_out)
+    s = (rms / (sigma_c * np.sqrt(M))).astype(np.float16)
+    target = (w.astype(np.float64) / s.astype(np.float64)[:, None]).astype(np.float32)
+    return w, s, target
+
+
 def gen_x(g: np.random.Generator, batch: int, d_in: int, dtype: str = "f16") -> np.ndarray:
     """Activations N(0,1): fp16 array for 'f16', uint16 bf16 bit patterns for 'bf16'."""
     v = g.standard_normal((batch, d_in))
