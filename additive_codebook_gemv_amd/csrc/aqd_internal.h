@@ -86,6 +86,11 @@ hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, cons
 hipError_t launch_split_reduce(const float* part, const uint16_t* scales, float* y, int64_t d_out, int batch,
                                int splits, hipStream_t s);
 hipError_t launch_zero_f32(float* y, int64_t n, hipStream_t s);
+hipError_t launch_zero_f16(uint16_t* y, int64_t n, hipStream_t s);
+// fp16 activations, fp16 output y = fp16(s * acc): the matrix-core route of the batch 2..8 GEMV
+hipError_t launch_gemm_sb_f16out(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                                 const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws,
+                                 hipStream_t s);
 // prefill / large batch (fp16 activations, fp32 output)
 size_t gemm_pf_workspace_bytes(const Geometry& g, int batch);
 hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     const uint8_t* __restrict__ packed, const uint4* __restrict__ codebooks, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ x, float* __restrict__ out, int64_t d_out, int64_t d_in, int64_t G,
     int64_t n_rt, int64_t plane_bytes, int batch, int chunks_per_split, int64_t n_chunks, int direct,
-    SbPlaneCols pc) {
+    SbPlaneCols pc, int out_f16) {
     constexpr int XP = XPlanes<MODE>::n;
     extern __shared__ __align__(16) uint8_t lds[];
     uint4* cb_lds = reinterpret_cast<uint4*>(lds);                        // [k][256] codewords
@@ -253,17 +253,19 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
         for (int q = 0; q < 4; ++q) {
             const int64_t i = it * TILE_ROWS + 4 * kq + q;
             if (i >= d_out) continue;
-            if (direct) out[(int64_t)col * d_out + i] = h2f(scales[i]) * acc[t][q];
-            else out[((int64_t)blockIdx.y * batch + col) * d_out + i] = acc[t][q];
+            if (!direct) out[((int64_t)blockIdx.y * batch + col) * d_out + i] = acc[t][q];
+            else if (out_f16) reinterpret_cast<uint16_t*>(out)[(int64_t)col * d_out + i] = f2h(h2f(scales[i]) * acc[t][q]);
+            else out[(int64_t)col * d_out + i] = h2f(scales[i]) * acc[t][q];
         }
     }
 }
 
-// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i].  Column n
-// is blockIdx.y; all the splits' partials are requested before any is added.
+// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i], fp32 or
+// (out_f16) rounded to fp16.  Column n is blockIdx.y; all the splits' partials
+// are requested before any is added.
 __global__ __launch_bounds__(256) void sb_reduce_kernel(const float* __restrict__ part,
-                                                        const uint16_t* __restrict__ scales, float* __restrict__ y,
-                                                        int64_t d_out, int batch, int splits) {
+                                                        const uint16_t* __restrict__ scales, void* __restrict__ y,
+                                                        int64_t d_out, int batch, int splits, int out_f16) {
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i >= d_out) return;
     const int64_t e = (int64_t)blockIdx.y * d_out + i;
@@ -275,7 +277,8 @@ __global__ __launch_bounds__(256) void sb_reduce_kernel(const float* __restrict_
 #pragma unroll
     for (int sp = 0; sp < SB_MAX_SPLITS; ++sp)
         if (sp < splits) acc += v[sp];
-    y[e] = h2f(scales[i]) * acc;
+    if (out_f16) static_cast<uint16_t*>(y)[e] = f2h(h2f(scales[i]) * acc);
+    else static_cast<float*>(y)[e] = h2f(scales[i]) * acc;
 }
 
 __global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
@@ -287,7 +290,19 @@ hipError_t launch_split_reduce(const float* part, const uint16_t* scales, float*
                                int splits, hipStream_t s) {
     if (splits > SB_MAX_SPLITS) return hipErrorInvalidValue;
     hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
-                       part, scales, y, d_out, batch, splits);
+                       part, scales, static_cast<void*>(y), d_out, batch, splits, 0);
+    return hipGetLastError();
+}
+
+__global__ void sb_zero16_kernel(uint16_t* __restrict__ y, int64_t n) {
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+        y[e] = 0;
+}
+
+hipError_t launch_zero_f16(uint16_t* y, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(sb_zero16_kernel, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256),
+                       0, s, y, n);
     return hipGetLastError();
 }
 
@@ -364,10 +379,11 @@ size_t gemm_sb_workspace_bytes(const Geometry& g, int batch) {
 template <int NT, int MODE, int K>
 static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
                            const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
-                           const SbPlaneCols& pc) {
+                           const SbPlaneCols& pc, int out_f16) {
     const SbPlan p = sb_plan(g, sb_per_cu<MODE>(K, batch));
     const int64_t n = (int64_t)batch * g.d_out;
-    if (p.n_chunks == 0) return launch_zero_f32(y, n, s);   // empty input: Y = 0
+    if (p.n_chunks == 0) return out_f16 ? launch_zero_f16(reinterpret_cast<uint16_t*>(y), n, s)
+                                        : launch_zero_f32(y, n, s);   // empty input: Y = 0
     const bool direct = p.splits == 1;
     constexpr size_t lds = sb_lds_bytes<MODE>(K, NT);
     static const hipError_t attr = hipFuncSetAttribute(
@@ -377,37 +393,40 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
     hipLaunchKernelGGL((gemm_sb_kernel<NT, MODE, K>), dim3((unsigned)p.wg_rows, (unsigned)p.splits),
                        dim3(64 * SB_WAVES), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
                        direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
-                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc);
+                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    return launch_split_reduce(static_cast<const float*>(ws), scales, y, g.d_out, batch, p.splits, s);
+    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((g.d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
+                       static_cast<const float*>(ws), scales, static_cast<void*>(y), g.d_out, batch, p.splits,
+                       out_f16);
+    return hipGetLastError();
 }
 
 template <int MODE, int K>
 static hipError_t launch_n(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales,
                            const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
-                           const SbPlaneCols& pc) {
+                           const SbPlaneCols& pc, int out_f16) {
     switch ((batch + 15) / 16) {
-        case 1: return launch_t<1, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 2: return launch_t<2, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 3: return launch_t<3, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        default: return launch_t<4, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 1: return launch_t<1, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 2: return launch_t<2, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 3: return launch_t<3, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        default: return launch_t<4, MODE, K>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
     }
 }
 
 template <int MODE>
 static hipError_t launch_m(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
                            const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s,
-                           const SbPlaneCols& pc) {
+                           const SbPlaneCols& pc, int out_f16 = 0) {
     switch (k) {
-        case 1: return launch_n<MODE, 1>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 2: return launch_n<MODE, 2>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 3: return launch_n<MODE, 3>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 4: return launch_n<MODE, 4>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 5: return launch_n<MODE, 5>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 6: return launch_n<MODE, 6>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        case 7: return launch_n<MODE, 7>(packed, cb, scales, x, y, batch, g, ws, s, pc);
-        default: return launch_n<MODE, 8>(packed, cb, scales, x, y, batch, g, ws, s, pc);
+        case 1: return launch_n<MODE, 1>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 2: return launch_n<MODE, 2>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 3: return launch_n<MODE, 3>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 4: return launch_n<MODE, 4>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 5: return launch_n<MODE, 5>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 6: return launch_n<MODE, 6>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        case 7: return launch_n<MODE, 7>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
+        default: return launch_n<MODE, 8>(packed, cb, scales, x, y, batch, g, ws, s, pc, out_f16);
     }
 }
 
@@ -419,6 +438,13 @@ hipError_t launch_gemm_sb(const uint8_t* packed, const uint16_t* codebooks, cons
     if (x_dt == AQD_F16) return launch_m<AQD_F16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
     if (x_dt == AQD_BF16X2) return launch_m<AQD_BF16X2>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
     return launch_m<AQD_BF16>(packed, codebooks, scales, k, xb, y, batch, g, ws, s, none);
+}
+
+hipError_t launch_gemm_sb_f16out(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                                 const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws,
+                                 hipStream_t s) {
+    const SbPlaneCols none = {};
+    return launch_m<AQD_F16>(packed, codebooks, scales, k, x, reinterpret_cast<float*>(y), batch, g, ws, s, none, 1);
 }
 
 hipError_t launch_gemm_sb_tiered(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales,

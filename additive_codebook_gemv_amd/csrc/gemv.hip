@@ -1,4 +1,6 @@
-// Decode GEMV, batch 1..8: lookup-and-accumulate over the packed code tiles.
+// Decode GEMV, batch 1..8: lookup-and-accumulate over the packed code tiles
+// (batch 1 through the table kernel, batch 2..8 with batch * k > 4 through the
+// fp16 matrix-core kernel, the rest here).
 //
 // Drop-by-Drop ("Multi-Bitwidth Quantization for LLMs Using Additive
 // Codebooks"), section 3.2: every 8-wide group of a weight row is the sum of
@@ -149,7 +151,18 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_direct_kernel(
     }
 }
 
-size_t gemv_workspace_bytes(const Geometry& g, int) { return gemv_lut_workspace_bytes(g); }
+// Batch 2..8 with batch * k > 4 goes to the fp16 matrix-core kernel: there its cost
+// (about the same for any batch up to 16) undercuts the 4 * batch dot products
+// per code of the direct kernel.
+static bool gemv_use_mfma(int batch, int k) { return batch >= 2 && batch * k > 4; }
+
+// The batch-1 accumulators (which must stay zero between calls) come first;
+// the matrix-core route's partial sums (overwritten by every call) follow.
+static size_t lut_region(const Geometry& g) { return (gemv_lut_workspace_bytes(g) + 255) & ~(size_t)255; }
+
+size_t gemv_workspace_bytes(const Geometry& g, int batch) {
+    return lut_region(g) + (batch >= 2 ? gemm_sb_workspace_bytes(g, batch) : 0);
+}
 
 template <int NB>
 static hipError_t launch_nb(const uint8_t* packed, const uint16_t* cb, const uint16_t* scales, int k,
@@ -164,6 +177,9 @@ static hipError_t launch_nb(const uint8_t* packed, const uint16_t* cb, const uin
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
     if (gemv_lut_supported(g, batch, k)) return launch_gemv_lut(packed, codebooks, scales, k, x, y, g, ws, s);
+    if (gemv_use_mfma(batch, k))
+        return launch_gemm_sb_f16out(packed, codebooks, scales, k, x, y, batch, g,
+                                     ws ? static_cast<uint8_t*>(ws) + lut_region(g) : nullptr, s);
     switch (batch) {
         case 1: return launch_nb<1>(packed, codebooks, scales, k, x, y, g, s);
         case 2: return launch_nb<2>(packed, codebooks, scales, k, x, y, g, s);

@@ -165,11 +165,15 @@ aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, 
  * y:            fp16 [batch][d_out].
  * k:            1..M.  batch: 1..8.
  * workspace:    device scratch of aqd_gemv_workspace_bytes(layer, batch) bytes
- *               (depends only on the layer; NULL allowed when it is 0).  It
- *               must be zero-filled before its first use; every successful call
- *               leaves the parts that must start at zero zeroed again, so one
- *               buffer serves any number of calls on one stream.  Calls that
- *               may overlap in time need separate workspaces.
+ *               (NULL allowed when it is 0).  It must be zero-filled before its
+ *               first use; every successful call leaves the parts that must
+ *               start at zero zeroed again, so one buffer of the largest size
+ *               needed serves any number of calls, at any batch, on one
+ *               stream.  Calls that may overlap in time need separate
+ *               workspaces.
+ * Batch 2..8 with batch * k > 4 runs on the matrix cores (the fp16 operand
+ * mode of aqd_gemm_small_batch, result rounded to fp16); the other cases use
+ * codeword lookups with v_dot2 accumulation.
  * Accumulation is fp32; the summation order is not specified, but it is fixed:
  * repeating a call on the same inputs gives the same bits.
  * packed_codes, x_rot and workspace 16-byte aligned; codebooks 16-byte aligned.

@@ -357,6 +357,18 @@ def test_gemv_workspace_reusable_and_deterministic(orc):
     assert torch.equal(outs[0], outs[2])       # same inputs, same bits
     ref = orc.forward(codes, cb, s, 2, x, lin.block)
     assert normwise(outs[3].cpu().numpy(), ref) <= TOL
+    # one buffer sized for batch 8 serves batch 8 (matrix-core route, partial sums after the batch-1
+    # region) and then batch 1: the batch-1 region is still zero and batch 1 gives the same bits
+    need8 = aqd.aqd_gemv_workspace_bytes(lin.d_out, lin.d_in, lin.M, 8)
+    assert need8 > need
+    ws8 = torch.zeros(need8, dtype=torch.uint8, device=dev())
+    x8 = aqd.aqd_hadamard_rotate(to_dev(wl.gen_x(wl.rng(42), 8, lin.d_in, "f16")), lin.block, aqd.AQD_F16)
+    y8 = aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, x8, lin.d_out, lin.d_in, 4, workspace=ws8)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws8[:need]).item() == 0
+    y1 = aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, xr, lin.d_out, lin.d_in, 4, workspace=ws8)
+    assert torch.equal(y1, outs[0])
+    assert torch.equal(aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, x8, lin.d_out, lin.d_in, 4, workspace=ws8), y8)
 
 
 def test_graph_replay_matches_eager(orc):
