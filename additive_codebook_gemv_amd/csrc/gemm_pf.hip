@@ -32,8 +32,15 @@ namespace aqd {
 typedef _Float16 pf_half8_t __attribute__((ext_vector_type(8)));
 typedef float pf_floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int PF_WAVES = 4;
-constexpr int PF_FRAGS = 4;                              // 16-row A fragments per wave
+#ifndef PF_WAVES_CFG
+#define PF_WAVES_CFG 8
+#endif
+#ifndef PF_PER_CU_CFG
+#define PF_PER_CU_CFG 1
+#endif
+constexpr int PF_WAVES = PF_WAVES_CFG;                   // waves per workgroup
+constexpr int PF_PER_CU = PF_PER_CU_CFG;                 // workgroups resident per compute unit
+constexpr int PF_FRAGS = 16 / PF_WAVES;                  // 16-row A fragments per wave
 constexpr int PF_TILES = PF_WAVES * PF_FRAGS;            // 16-row code tiles per workgroup (256 rows)
 constexpr int PF_CHUNK = 64;                             // inputs per staged chunk (8 groups)
 constexpr int PF_CHUNK_GROUPS = PF_CHUNK / GROUP;
@@ -77,7 +84,7 @@ struct PfLds {
 };
 
 template <int K, int NB>
-__global__ __launch_bounds__(64 * PF_WAVES) void gemm_pf_kernel(PfArgs p) {
+__global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_pf_kernel(PfArgs p) {
     using L = PfLds<K, NB>;
     __shared__ __align__(16) uint4 cb_lds[K * CODEWORDS];                 // [K][256] codewords
     __shared__ __align__(16) uint8_t x0[L::XB];
@@ -105,7 +112,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pf_kernel(PfArgs p) {
     // Codes: one wave instruction moves 8 row tiles x 8 groups of one plane.
     auto stage = [&](int64_t ch, uint8_t* xd, uint8_t* kd) {
 #pragma unroll
-        for (int q = 0; q < NB / 2; ++q) {
+        for (int q = 0; q < 2 * NB / PF_WAVES; ++q) {
             const int blk = q * PF_WAVES + wave;                           // 8-column block
             const int col = blk * 8 + (lane >> 3);
             const int piece = (lane & 7) ^ ((col >> 1) & 7);
@@ -220,7 +227,10 @@ __global__ __launch_bounds__(64 * PF_WAVES) void gemm_pf_kernel(PfArgs p) {
 
 // B fragments per wave: 128 batch columns per workgroup.  (Wider tiles need more
 // than the 256 accumulator registers a wave has once the loop carries two chunks.)
-constexpr int PF_NB = 8;
+#ifndef PF_NB_CFG
+#define PF_NB_CFG 8
+#endif
+constexpr int PF_NB = PF_NB_CFG;
 
 struct PfPlan {
     int64_t n_chunks, row_blocks, col_blocks;
@@ -243,7 +253,7 @@ static PfPlan pf_plan(const Geometry& g, int batch) {
     for (int64_t sp = 1; sp <= PF_MAX_SPLITS && sp <= p.n_chunks; ++sp) {
         const int64_t cps = (p.n_chunks + sp - 1) / sp;
         const int64_t used = (p.n_chunks + cps - 1) / cps;
-        const int64_t cost = ((tiles * used + 255) / 256) * cps;
+        const int64_t cost = ((tiles * used + 256 * PF_PER_CU - 1) / (256 * PF_PER_CU)) * cps;
         if (best < 0 || cost < best) {
             best = cost;
             p.splits = (int)used;
