@@ -153,6 +153,9 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
             // (and their registers) above this step's products
             __builtin_amdgcn_sched_barrier(0);
             // this lane's group exists and belongs to this split (not the trailing padding chunk)
+            // (inputs past d_in and the padding chunk already hold zero activations; the weights there are
+            // zeroed too, in the rare chunks that have any, so no stray codeword meets them)
+            const bool whole = ch < c1 && (ch + 1) * PF_CHUNK_GROUPS <= p.G;           // uniform
             const bool valid = ch < c1 && ch * PF_CHUNK_GROUPS + 4 * s + kq < p.G;
             pf_half8_t a[PF_FRAGS];
 #pragma unroll
@@ -172,7 +175,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
                         w[3] = pf_u32(pf_h2(w[3]) + pf_h2(c.w));
                     }
                 }
-                const uint4 wv = valid ? make_uint4(w[0], w[1], w[2], w[3]) : make_uint4(0u, 0u, 0u, 0u);
+                uint4 wv = make_uint4(w[0], w[1], w[2], w[3]);
+                if (!whole && !valid) wv = make_uint4(0u, 0u, 0u, 0u);
                 a[f] = __builtin_bit_cast(pf_half8_t, wv);
             }
 #pragma unroll
@@ -225,12 +229,13 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
     }
 }
 
-// B fragments per wave: 128 batch columns per workgroup.  (Wider tiles need more
-// than the 256 accumulator registers a wave has once the loop carries two chunks.)
-#ifndef PF_NB_CFG
-#define PF_NB_CFG 8
-#endif
-constexpr int PF_NB = PF_NB_CFG;
+// B fragments per wave (16 batch columns each).  128 columns by default; 256 where
+// they measured faster (batch >= 512 over a long input dimension, k <= 4: more
+// codebooks would spill), which doubles the accumulators and halves the
+// codeword gathers per product.
+static int pf_nb(const Geometry& g, int batch, int k) {
+    return batch >= 512 && g.d_in >= 8192 && k <= 4 ? 16 : 8;
+}
 
 struct PfPlan {
     int64_t n_chunks, row_blocks, col_blocks;
@@ -240,11 +245,11 @@ struct PfPlan {
 // Splits of the input dimension: the smallest split count that minimises
 // (rounds of workgroups over the 256 compute units) x (chunks per split), one
 // workgroup per compute unit; at most PF_MAX_SPLITS.
-static PfPlan pf_plan(const Geometry& g, int batch) {
+static PfPlan pf_plan(const Geometry& g, int batch, int k) {
     PfPlan p;
     p.n_chunks = (g.d_in + PF_CHUNK - 1) / PF_CHUNK;
     p.row_blocks = (g.n_rt + PF_TILES - 1) / PF_TILES;
-    p.col_blocks = (batch + PF_NB * 16 - 1) / (PF_NB * 16);
+    p.col_blocks = (batch + pf_nb(g, batch, k) * 16 - 1) / (pf_nb(g, batch, k) * 16);
     p.splits = 1;
     p.chunks_per_split = (int)p.n_chunks;
     const int64_t tiles = p.row_blocks * p.col_blocks;
@@ -264,8 +269,13 @@ static PfPlan pf_plan(const Geometry& g, int batch) {
 }
 
 size_t gemm_pf_workspace_bytes(const Geometry& g, int batch) {
-    const PfPlan p = pf_plan(g, batch);
-    return p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4 : 0;
+    size_t need = 0;                                   // the largest over k
+    for (int k = 1; k <= g.M && k <= MAX_M; ++k) {
+        const PfPlan p = pf_plan(g, batch, k);
+        const size_t b = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4 : 0;
+        need = b > need ? b : need;
+    }
+    return need;
 }
 
 template <int K, int NB>
@@ -292,7 +302,7 @@ static hipError_t launch_pf_k(int k, const PfArgs& a, const PfPlan& pl, hipStrea
 
 hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                           const uint16_t* x, float* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
-    const PfPlan pl = pf_plan(g, batch);
+    const PfPlan pl = pf_plan(g, batch, k);
     if (pl.n_chunks == 0) return launch_zero_f32(y, (int64_t)batch * g.d_out, s);   // empty input: Y = 0
     PfArgs a;
     a.packed = packed;
@@ -309,7 +319,7 @@ hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, cons
     a.n_chunks = pl.n_chunks;
     a.batch = batch;
     a.chunks_per_split = pl.chunks_per_split;
-    const hipError_t e = launch_pf_k<PF_NB>(k, a, pl, s);
+    const hipError_t e = pf_nb(g, batch, k) == 16 ? launch_pf_k<16>(k, a, pl, s) : launch_pf_k<8>(k, a, pl, s);
     if (e != hipSuccess || a.direct) return e;
     return launch_split_reduce(static_cast<const float*>(ws), scales, y, g.d_out, batch, pl.splits, s);
 }

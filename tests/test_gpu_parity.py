@@ -589,6 +589,7 @@ def test_small_batch_tiered_edge(orc):
     (17, 64, 2, (1, 5, 129)),         # one chunk, rows inside one fragment
     (512, 960, 4, (128,)),            # 15 chunks split one per workgroup: odd chunk counts per split
     (33, 8, 8, (3,)),                 # one group, M = 8, every k
+    (600, 8192, 4, (520,)),           # 256-column tiles (batch >= 512, long inputs): ragged rows and columns
 ])
 def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(51, extra=d_out * 7 + d_in + M)
