@@ -708,3 +708,72 @@ def test_encode_full_size_sampled_and_decoded(orc):
         errs.append(np.linalg.norm(wk - w[rows].astype(np.float64)) / np.linalg.norm(w[rows]))
     record(test="encode_error_curve", rel_err=errs)
     assert all(a > b for a, b in zip(errs, errs[1:])), errs
+
+
+# ---------------------------------------------------------------------------
+# seeded random shapes across the entry points
+# ---------------------------------------------------------------------------
+
+def _random_case(seed: int, block_multiple: int = 8):
+    g = np.random.Generator(np.random.PCG64(0xF00D + seed))
+    d_out = int(g.integers(1, 700))
+    d_in = int(g.integers(1, 1600 // block_multiple)) * block_multiple
+    M = int(g.integers(1, 9))
+    k = int(g.integers(1, M + 1))
+    gg = wl.rng(81, extra=seed)
+    return g, d_out, d_in, M, k, wl.gen_codes(gg, d_out, d_in, M), wl.gen_codebooks(gg, M), wl.gen_scales(gg, d_out)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shapes_gemv_small_batch_prefill(orc, seed):
+    """Random d_out (1..699), d_in (8..1592), M (1..8), k and batch: the GEMV (batch 1..8), the small batch
+    (1..64) and the prefill (1..300) against the oracle on the same inputs."""
+    g, d_out, d_in, M, k, codes, cb, s = _random_case(seed)
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    bg, bs, bp = int(g.integers(1, 9)), int(g.integers(1, 65)), int(g.integers(1, 301))
+    x = wl.gen_x(wl.rng(82, extra=seed), max(bg, bs, bp), d_in, "f16")
+    ref = orc.linear(codes, cb, s, k, x)
+    cases = (
+        ("gemv", bg, lambda: aqd.aqd_gemv(packed, cbdev, sdev, k, to_dev(x[:bg]), d_out, d_in, M)),
+        ("small_batch", bs, lambda: aqd.aqd_gemm_small_batch(packed, cbdev, sdev, k, to_dev(x[:bs]), d_out, d_in, M,
+                                                             aqd.AQD_F16)),
+        ("prefill", bp, lambda: aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(x[:bp]), d_out, d_in, M)),
+    )
+    for name, B, fn in cases:
+        y = fn().float().cpu().numpy()
+        e = normwise(y, ref[:B])
+        record(test="random_" + name, shape=[d_out, d_in, M], k=k, batch=B, err=e)
+        assert e <= TOL, (name, d_out, d_in, M, k, B, e)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_shapes_rotating_grouped(orc, seed):
+    """Random groups of 1..4 linears sharing an input of random width (a multiple of the block), plain or
+    with a sign mask: the launch that rotates its own input against the oracle's rotation and product."""
+    g = np.random.Generator(np.random.PCG64(0xBEEF + seed))
+    block = int(g.choice([64, 128, 256]))
+    d_in = int(g.integers(1, 2048 // block + 1)) * block
+    n = int(g.integers(1, 5))
+    M = int(g.integers(1, 9))
+    k = int(g.integers(1, M + 1))
+    signed = bool(seed % 2)
+    gg = wl.rng(83, extra=seed)
+    x = wl.gen_x(gg, 1, d_in, "f16")
+    signs = wl.gen_signs(gg, d_in)
+    xrot = orc.rotate_signed(x, signs, block) if signed else orc.rotate(x, block)
+    lins, refs = [], []
+    for _ in range(n):
+        d_out = int(g.integers(1, 900))
+        codes, cb, s = wl.gen_codes(gg, d_out, d_in, M), wl.gen_codebooks(gg, M), wl.gen_scales(gg, d_out)
+        cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+        lins.append((aqd.aqd_pack_codes(cdev), cbdev, sdev, d_out, M))
+        refs.append(orc.linear(codes, cb, s, k, xrot))
+    if signed:
+        ys = aqd.aqd_rotate_gemv_grouped_signed(lins, k, to_dev(x), d_in, block, to_dev(signs))
+    else:
+        ys = aqd.aqd_rotate_gemv_grouped(lins, k, to_dev(x), d_in, block)
+    for y, ref, lin in zip(ys, refs, lins):
+        e = normwise(y.float().cpu().numpy(), ref)
+        record(test="random_rotating_grouped", d_out=lin[3], d_in=d_in, M=M, k=k, block=block, signed=signed, err=e)
+        assert e <= TOL, (lin[3], d_in, M, k, block, signed, e)
