@@ -100,6 +100,14 @@ hipError_t launch_gemm_pf(const uint8_t* packed, const uint16_t* codebooks, cons
 hipError_t launch_encode_greedy(const float* target, const uint16_t* codebooks, int M, int64_t d_out,
                                 int64_t d_in, uint8_t* codes, hipStream_t s);
 
+// Split partial sums, shared by the small-batch and prefill kernels and their
+// reduce: [split][column][row quad] of float4 (rows 4q .. 4q+3).  The lanes that
+// hold consecutive row quads of one column write one contiguous run, and a
+// reduce thread reads each split's quad as one 16-byte word.
+inline size_t partial_bytes(int64_t d_out, int batch, int splits) {
+    return (size_t)splits * (size_t)batch * (size_t)((d_out + 3) / 4) * 16;
+}
+
 // ---- device helpers --------------------------------------------------------
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -117,6 +125,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even, N
     if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void store_partial(float* part, int64_t d_out, int batch, unsigned split, int col,
+                                              int64_t row0, float4 v) {
+    const int64_t nq = (d_out + 3) / 4;
+    reinterpret_cast<float4*>(part)[((int64_t)split * batch + col) * nq + row0 / 4] = v;
 }
 
 }  // namespace aqd

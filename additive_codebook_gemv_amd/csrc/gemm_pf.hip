@@ -217,13 +217,16 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
             const int col = col0 + t * 16 + r;
-            if (col >= p.batch) continue;
+            if (col >= p.batch || row0 >= p.d_out) continue;
+            if (!p.direct) {          // one 16-byte partial per (column, row quad, split)
+                store_partial(p.out, p.d_out, p.batch, blockIdx.z, col, row0,
+                              make_float4(acc[f][t][0], acc[f][t][1], acc[f][t][2], acc[f][t][3]));
+                continue;
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int64_t i = row0 + q;
-                if (i >= p.d_out) continue;
-                if (p.direct) p.out[(int64_t)col * p.d_out + i] = h2f(p.scales[i]) * acc[f][t][q];
-                else p.out[((int64_t)blockIdx.z * p.batch + col) * p.d_out + i] = acc[f][t][q];
+                if (i < p.d_out) p.out[(int64_t)col * p.d_out + i] = h2f(p.scales[i]) * acc[f][t][q];
             }
         }
     }
@@ -272,7 +275,7 @@ size_t gemm_pf_workspace_bytes(const Geometry& g, int batch) {
     size_t need = 0;                                   // the largest over k
     for (int k = 1; k <= g.M && k <= MAX_M; ++k) {
         const PfPlan p = pf_plan(g, batch, k);
-        const size_t b = p.splits > 1 ? (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4 : 0;
+        const size_t b = p.splits > 1 ? partial_bytes(g.d_out, batch, p.splits) : 0;
         need = b > need ? b : need;
     }
     return need;

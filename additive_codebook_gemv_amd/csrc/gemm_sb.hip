@@ -249,36 +249,57 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     for (int t = 0; t < NT; ++t) {
         const int col = t * 16 + r;
         if (col >= batch) continue;
+        const int64_t row0 = it * TILE_ROWS + 4 * kq;
+        if (!direct) {            // one 16-byte partial per (column, row quad, split)
+            if (row0 < d_out)
+                store_partial(out, d_out, batch, blockIdx.y, col, row0,
+                              make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]));
+            continue;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int64_t i = it * TILE_ROWS + 4 * kq + q;
+            const int64_t i = row0 + q;
             if (i >= d_out) continue;
-            if (!direct) out[((int64_t)blockIdx.y * batch + col) * d_out + i] = acc[t][q];
-            else if (out_f16) reinterpret_cast<uint16_t*>(out)[(int64_t)col * d_out + i] = f2h(h2f(scales[i]) * acc[t][q]);
+            if (out_f16) reinterpret_cast<uint16_t*>(out)[(int64_t)col * d_out + i] = f2h(h2f(scales[i]) * acc[t][q]);
             else out[(int64_t)col * d_out + i] = h2f(scales[i]) * acc[t][q];
         }
     }
 }
 
-// y[n][i] = s_i * sum over splits (fixed order) of part[split][n][i], fp32 or
-// (out_f16) rounded to fp16.  Column n is blockIdx.y; all the splits' partials
-// are requested before any is added.
-__global__ __launch_bounds__(256) void sb_reduce_kernel(const float* __restrict__ part,
+// y[n][i] = s_i * sum over splits (fixed order) of the partials, fp32 or
+// (out_f16) rounded to fp16.  Thread (row quad, column n = blockIdx.y) reads one
+// 16-byte word per split, all requested before any is added.
+constexpr int SB_REDUCE_THREADS = 64;   // small blocks: the work is latency-bound, spread it over many CUs
+
+__global__ __launch_bounds__(SB_REDUCE_THREADS) void sb_reduce_kernel(const float* __restrict__ part,
                                                         const uint16_t* __restrict__ scales, void* __restrict__ y,
                                                         int64_t d_out, int batch, int splits, int out_f16) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i >= d_out) return;
-    const int64_t e = (int64_t)blockIdx.y * d_out + i;
-    const int64_t n = (int64_t)batch * d_out;
-    float v[SB_MAX_SPLITS];
+    const int64_t q4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    const int64_t nq = (d_out + 3) / 4;
+    if (q4 >= nq) return;
+    const float4* pq = reinterpret_cast<const float4*>(part) + (int64_t)blockIdx.y * nq + q4;
+    const int64_t stride = (int64_t)batch * nq;                 // one split to the next
+    float4 v[SB_MAX_SPLITS];
 #pragma unroll
-    for (int sp = 0; sp < SB_MAX_SPLITS; ++sp) v[sp] = part[(sp < splits ? sp : 0) * n + e];
-    float acc = 0.f;
+    for (int sp = 0; sp < SB_MAX_SPLITS; ++sp) v[sp] = pq[(sp < splits ? sp : 0) * stride];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int sp = 0; sp < SB_MAX_SPLITS; ++sp)
-        if (sp < splits) acc += v[sp];
-    if (out_f16) static_cast<uint16_t*>(y)[e] = f2h(h2f(scales[i]) * acc);
-    else static_cast<float*>(y)[e] = h2f(scales[i]) * acc;
+        if (sp < splits) {
+            a.x += v[sp].x;
+            a.y += v[sp].y;
+            a.z += v[sp].z;
+            a.w += v[sp].w;
+        }
+    const float sum[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t i = 4 * q4 + c;
+        if (i >= d_out) break;
+        const int64_t e = (int64_t)blockIdx.y * d_out + i;
+        if (out_f16) static_cast<uint16_t*>(y)[e] = f2h(h2f(scales[i]) * sum[c]);
+        else static_cast<float*>(y)[e] = h2f(scales[i]) * sum[c];
+    }
 }
 
 __global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
@@ -289,8 +310,9 @@ __global__ void sb_zero_kernel(float* __restrict__ y, int64_t n) {
 hipError_t launch_split_reduce(const float* part, const uint16_t* scales, float* y, int64_t d_out, int batch,
                                int splits, hipStream_t s) {
     if (splits > SB_MAX_SPLITS) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
-                       part, scales, static_cast<void*>(y), d_out, batch, splits, 0);
+    hipLaunchKernelGGL(sb_reduce_kernel,
+                       dim3((unsigned)(((d_out + 3) / 4 + SB_REDUCE_THREADS - 1) / SB_REDUCE_THREADS), (unsigned)batch),
+                       dim3(SB_REDUCE_THREADS), 0, s, part, scales, static_cast<void*>(y), d_out, batch, splits, 0);
     return hipGetLastError();
 }
 
@@ -369,7 +391,7 @@ size_t gemm_sb_workspace_bytes(const Geometry& g, int batch) {
         for (int dt : {AQD_F16, AQD_BF16X2}) {
             const SbPlan p = sb_plan_for(g, k, batch, dt);
             if (p.splits > 1) {
-                const size_t b = (size_t)p.splits * (size_t)batch * (size_t)g.d_out * 4;
+                const size_t b = partial_bytes(g.d_out, batch, p.splits);
                 need = b > need ? b : need;
             }
         }
@@ -396,9 +418,11 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                        p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
-    hipLaunchKernelGGL(sb_reduce_kernel, dim3((unsigned)((g.d_out + 255) / 256), (unsigned)batch), dim3(256), 0, s,
-                       static_cast<const float*>(ws), scales, static_cast<void*>(y), g.d_out, batch, p.splits,
-                       out_f16);
+    hipLaunchKernelGGL(sb_reduce_kernel,
+                       dim3((unsigned)(((g.d_out + 3) / 4 + SB_REDUCE_THREADS - 1) / SB_REDUCE_THREADS),
+                            (unsigned)batch),
+                       dim3(SB_REDUCE_THREADS), 0, s, static_cast<const float*>(ws), scales, static_cast<void*>(y),
+                       g.d_out, batch, p.splits, out_f16);
     return hipGetLastError();
 }
 
