@@ -245,9 +245,9 @@ struct PfPlan {
     int splits, chunks_per_split;
 };
 
-// Splits of the input dimension: the smallest split count that minimises
-// (rounds of workgroups over the 256 compute units) x (chunks per split), one
-// workgroup per compute unit; at most PF_MAX_SPLITS.
+// Splits of the input dimension, only when the tiles do not cover the 256
+// compute units: the smallest split count that minimises (rounds of workgroups
+// over the chip) x (chunks per split); at most PF_MAX_SPLITS.
 static PfPlan pf_plan(const Geometry& g, int batch, int k) {
     PfPlan p;
     p.n_chunks = (g.d_in + PF_CHUNK - 1) / PF_CHUNK;
@@ -257,6 +257,9 @@ static PfPlan pf_plan(const Geometry& g, int batch, int k) {
     p.chunks_per_split = (int)p.n_chunks;
     const int64_t tiles = p.row_blocks * p.col_blocks;
     if (tiles == 0 || p.n_chunks == 0) return p;
+    // Tiles that cover the chip on their own are not split: the reduce of the partials (a full fp32
+    // copy of Y per split, read back) costs more than the last round's idle CUs.
+    if (tiles >= 256 * PF_PER_CU) return p;
     int64_t best = -1;
     for (int64_t sp = 1; sp <= PF_MAX_SPLITS && sp <= p.n_chunks; ++sp) {
         const int64_t cps = (p.n_chunks + sp - 1) / sp;
