@@ -45,7 +45,8 @@ constexpr int LUT_PAIR_BYTES = CODEWORDS * 64 * 4;           // 64 KiB
 constexpr int LUT_BYTES = (LUT_SLOTS / 2) * LUT_PAIR_BYTES;  // 128 KiB
 constexpr int LUT_CUS = 256;                                  // one 128 KiB workgroup per CU
 constexpr int LUT_WAVES = 16;
-constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles a wave keeps in flight
+constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles per wave, default
+constexpr int LUT_TILES_PER_WAVE_BIG = 4;                     // ... when 2 would need more workgroups than CUs
 constexpr int LUT_MAX_GROUP = AQD_MAX_GROUP;                  // linears per launch
 
 // One linear of a launch.  Several linears that share the input (and k) run
@@ -145,7 +146,7 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
 // Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
 // butterflies and rounding of the standalone rotation (same bits), after the
 // optional sign flips of the randomized variant.
-template <int WAVES, int K, bool MULTI, int HB>
+template <int WAVES, int K, bool MULTI, int HB, int TPW>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     constexpr int XS_BYTES = HB > 0 ? LUT_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
     __shared__ __align__(16) uint8_t lds[LUT_BYTES + XS_BYTES + 16];
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     // stream is in flight while the tables are built.  The second half is
     // requested only after the build (below): requests issued earlier would sit
     // in front of other workgroups' table operands and delay every build.
-    uint4 codes[LUT_TILES_PER_WAVE][LUT_SLOTS];
+    uint4 codes[TPW][LUT_SLOTS];
     auto load_tile = [&](int u) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
         const uint32_t off = it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE;
@@ -249,9 +250,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     };
     load_tile(0);
     // scales of the rows this lane may finish (needed only at the end; clamped)
-    uint16_t row_scale[LUT_TILES_PER_WAVE];
+    uint16_t row_scale[TPW];
 #pragma unroll
-    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
         row_scale[u] = L.scales[row < L.d_out ? row : L.d_out - 1];
     }
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 1; u < LUT_TILES_PER_WAVE; ++u) load_tile(u);
+    for (int u = 1; u < TPW; ++u) load_tile(u);
 
     uint32_t base[LUT_SLOTS];
 #pragma unroll
@@ -313,16 +314,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 
     // returned accumulator words are examined only after the last tile, so the
     // atomics' round trips overlap the remaining lookups
-    unsigned long long old_word[LUT_TILES_PER_WAVE], term[LUT_TILES_PER_WAVE];
-    bool mine[LUT_TILES_PER_WAVE];
+    unsigned long long old_word[TPW], term[TPW];
+    bool mine[TPW];
 #pragma unroll
-    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         mine[u] = false;
         old_word[u] = 0ull;
         term[u] = 0ull;
     }
 #pragma unroll
-    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
         if (it >= t1) break;                   // uniform across the wave
         float rows[16];
@@ -352,7 +353,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
         }
     }
 #pragma unroll
-    for (int u = 0; u < LUT_TILES_PER_WAVE; ++u) {
+    for (int u = 0; u < TPW; ++u) {
         if (!mine[u] || !fix_is_last(old_word[u], p.slices)) continue;
         // this lane added the last contribution of its row: it holds the complete sum
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
@@ -368,8 +369,8 @@ static int lut_slices(int64_t n_gt, int k) { return (int)(((int64_t)k * n_gt + L
 
 // Row tiles per workgroup for each linear: the grid aims at one workgroup per
 // CU, shared among the linears in proportion to their rows; a workgroup holds
-// at most LUT_WAVES * LUT_TILES_PER_WAVE tiles.
-static void lut_plan(const int64_t* n_rt, int n, int slices, int* tpb, int* blocks) {
+// at most LUT_WAVES * tiles_per_wave tiles.
+static void lut_plan(const int64_t* n_rt, int n, int slices, int tiles_per_wave, int* tpb, int* blocks) {
     int64_t total = 0;
     for (int i = 0; i < n; ++i) total += n_rt[i];
     for (int i = 0; i < n; ++i) {
@@ -377,7 +378,7 @@ static void lut_plan(const int64_t* n_rt, int n, int slices, int* tpb, int* bloc
         if (rb < 1) rb = 1;
         if (rb > n_rt[i]) rb = n_rt[i];
         int64_t t = (n_rt[i] + rb - 1) / rb;
-        if (t > LUT_WAVES * LUT_TILES_PER_WAVE) t = LUT_WAVES * LUT_TILES_PER_WAVE;
+        if (t > LUT_WAVES * tiles_per_wave) t = LUT_WAVES * tiles_per_wave;
         tpb[i] = (int)t;
         blocks[i] = (int)((n_rt[i] + t - 1) / t);
     }
@@ -402,18 +403,24 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
     return b;
 }
 
-template <bool MULTI, int HB>
+template <bool MULTI, int HB, int TPW>
 static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
     switch (k) {
-        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB>), gd, bd, 0, s, a); break;
-        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB>), gd, bd, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB>), gd, bd, 0, s, a); break;
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
     }
+}
+
+template <bool MULTI, int HB>
+static void launch_tpw(int tpw, int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
+    if (tpw == LUT_TILES_PER_WAVE_BIG) launch_k<MULTI, HB, LUT_TILES_PER_WAVE_BIG>(k, gd, bd, s, a);
+    else launch_k<MULTI, HB, LUT_TILES_PER_WAVE>(k, gd, bd, s, a);
 }
 
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
@@ -445,7 +452,15 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
         }
     if (m == 0) return hipSuccess;
     a.n_lin = m;
-    lut_plan(n_rt, m, a.slices, tpb, blocks);
+    // two row tiles per wave, or four when two would need more workgroups than CUs (a second round)
+    int tpw = LUT_TILES_PER_WAVE;
+    lut_plan(n_rt, m, a.slices, tpw, tpb, blocks);
+    int64_t wgs = 0;
+    for (int i = 0; i < m; ++i) wgs += (int64_t)a.slices * blocks[i];
+    if (wgs > LUT_CUS) {
+        tpw = LUT_TILES_PER_WAVE_BIG;
+        lut_plan(n_rt, m, a.slices, tpw, tpb, blocks);
+    }
     uint8_t* acc = static_cast<uint8_t*>(ws);
     int wg = 0;
     for (int i = 0; i < m; ++i) {
@@ -456,11 +471,11 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
         wg += a.slices * blocks[i];
     }
     const dim3 gd((unsigned)wg), bd(64 * LUT_WAVES);
-    if (rotate_block == 64) launch_k<true, 64>(k, gd, bd, s, a);
-    else if (rotate_block == 128) launch_k<true, 128>(k, gd, bd, s, a);
-    else if (rotate_block == 256) launch_k<true, 256>(k, gd, bd, s, a);
-    else if (m == 1) launch_k<false, 0>(k, gd, bd, s, a);
-    else launch_k<true, 0>(k, gd, bd, s, a);
+    if (rotate_block == 64) launch_tpw<true, 64>(tpw, k, gd, bd, s, a);
+    else if (rotate_block == 128) launch_tpw<true, 128>(tpw, k, gd, bd, s, a);
+    else if (rotate_block == 256) launch_tpw<true, 256>(tpw, k, gd, bd, s, a);
+    else if (m == 1) launch_tpw<false, 0>(tpw, k, gd, bd, s, a);
+    else launch_tpw<true, 0>(tpw, k, gd, bd, s, a);
     return hipGetLastError();
 }
 

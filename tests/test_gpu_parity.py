@@ -426,6 +426,7 @@ def test_graph_replay_matches_eager(orc):
 @pytest.mark.parametrize("shapes,d_in,k", [
     ([4096, 1024, 1024], 4096, 3),           # q, k, v of the 8B-shaped stack
     ([14336, 14336], 4096, 2),               # gate, up
+    ([14336, 14336], 4096, 4),               # gate, up with four row tiles per wave (one round of workgroups)
     ([1000, 0, 33, 16], 1000, 2),            # ragged rows and groups, an empty linear, four linears
 ])
 def test_grouped_gemv_matches_separate_calls(orc, shapes, d_in, k):
@@ -457,6 +458,7 @@ def test_grouped_gemv_matches_separate_calls(orc, shapes, d_in, k):
 @pytest.mark.parametrize("shapes,d_in,block,k", [
     ([4096, 1024, 1024], 4096, 128, 3),     # q, k, v with their rotation
     ([4096], 14336, 256, 4),                 # down projection
+    ([14336, 14336], 4096, 128, 3),          # gate, up with four row tiles per wave
     ([300, 17], 576, 64, 2),                 # ragged rows, a partial group tile, block 64
     ([64], 256, 256, 1),
 ])
