@@ -40,8 +40,8 @@ CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 an
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
 # only for the kernel source they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30690693
-TRAFFIC_K4_SOURCE_SHA256_PREFIX = "e073062abc1b0b94"
+TRAFFIC_K4_BYTES = 30690154
+TRAFFIC_K4_SOURCE_SHA256_PREFIX = "b13dcc340405bec4"
 
 
 def measured_traffic():
