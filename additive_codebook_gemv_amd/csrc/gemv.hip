@@ -156,9 +156,13 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_direct_kernel(
 // per code of the direct kernel.
 static bool gemv_use_mfma(int batch, int k) { return batch >= 2 && batch * k > 4; }
 
-// The batch-1 accumulators (which must stay zero between calls) come first;
-// the matrix-core route's partial sums (overwritten by every call) follow.
-static size_t lut_region(const Geometry& g) { return (gemv_lut_workspace_bytes(g) + 255) & ~(size_t)255; }
+// The lookup-table accumulators of batch 1 and 2 (which must stay zero between
+// calls) come first; the matrix-core route's partial sums (overwritten by every
+// call) follow.
+static size_t lut_region(const Geometry& g) {
+    const size_t b1 = gemv_lut_workspace_bytes(g), b2 = gemv_lut2_workspace_bytes(g);
+    return ((b1 > b2 ? b1 : b2) + 255) & ~(size_t)255;
+}
 
 size_t gemv_workspace_bytes(const Geometry& g, int batch) {
     return lut_region(g) + (batch >= 2 ? gemm_sb_workspace_bytes(g, batch) : 0);
@@ -177,6 +181,7 @@ static hipError_t launch_nb(const uint8_t* packed, const uint16_t* cb, const uin
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
     if (gemv_lut_supported(g, batch, k)) return launch_gemv_lut(packed, codebooks, scales, k, x, y, g, ws, s);
+    if (gemv_lut2_supported(g, batch, k)) return launch_gemv_lut2(packed, codebooks, scales, k, x, y, g, ws, s);
     if (gemv_use_mfma(batch, k))
         return launch_gemm_sb_f16out(packed, codebooks, scales, k, x, y, batch, g,
                                      ws ? static_cast<uint8_t*>(ws) + lut_region(g) : nullptr, s);

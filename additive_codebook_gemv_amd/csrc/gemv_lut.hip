@@ -32,21 +32,11 @@
 // it by s_i, rounds to fp16, writes y and clears the word.  No barrier or
 // counter is needed, results are bit-reproducible, and the workspace is zero
 // again when the kernel ends.
-#include "fixed_sum.h"
 #include "fwht_device.h"
+#include "lut_device.h"
 
 namespace aqd {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float floatx16_t __attribute__((ext_vector_type(16)));
-
-constexpr int LUT_SLOTS = 4;
-constexpr int LUT_PAIR_BYTES = CODEWORDS * 64 * 4;           // 64 KiB
-constexpr int LUT_BYTES = (LUT_SLOTS / 2) * LUT_PAIR_BYTES;  // 128 KiB
-constexpr int LUT_CUS = 256;                                  // one 128 KiB workgroup per CU
-constexpr int LUT_WAVES = 16;
-constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles per wave, default
-constexpr int LUT_TILES_PER_WAVE_BIG = 4;                     // ... when 2 would need more workgroups than CUs
 constexpr int LUT_MAX_GROUP = AQD_MAX_GROUP;                  // linears per launch
 
 // One linear of a launch.  Several linears that share the input (and k) run
@@ -69,78 +59,6 @@ struct LutArgs {
     int k, n_slots, slices, n_lin;
     const uint64_t* signs;       // rotating launch only: NULL or the input sign mask (bit c of word c / 64)
 };
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over the row tiles of one slot (the dword-3 format word of
-// the gfx9 family for raw byte-addressed buffers).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(const uint8_t* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-// Streaming 16-byte load of codes that are read exactly once (nontemporal).
-// An offset past the end of the descriptor returns zeros without touching
-// memory, which is how a wave without a tile keeps its load count fixed.
-constexpr uint32_t NO_TILE = 0x80000000u;
-__device__ __forceinline__ uint4 load_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
-
-__device__ __forceinline__ uint32_t lut_addr(uint32_t code_dword, uint32_t base, int byte) {
-    // byte 0 <- base byte 0 (lane offset), byte 1 <- code byte `byte`, byte 2 <- base byte 2 (slot pair)
-    return __builtin_amdgcn_perm(code_dword, base, 0x0C020000u | ((uint32_t)(4 + byte) << 8));
-}
-
-// Row sums travel between workgroups as counted fixed-point words (fixed_sum.h).
-constexpr int LUT_MAX_SLICES = FIX_MAX_TERMS;
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ float2 swap32(float a, float b) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float2 swap16(float a, float b) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// v[r] = partial of row r in this lane.  Returns, in lane l, the sum over the
-// 64 lanes of row (l >> 2).
-__device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
-    float a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {          // lanes 0-31 keep row i, lanes 32-63 keep row i+8
-        const float2 s = swap32(v[i], v[i + 8]);
-        a[i] = s.x + s.y;
-    }
-    float b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {          // even 16-lane rows keep i, odd rows keep i+4
-        const float2 s = swap16(a[i], a[i + 4]);
-        b[i] = s.x + s.y;
-    }
-    const bool lo8 = (lane & 8) == 0;      // partner lane j <-> 15-j inside 16 lanes
-    float c[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float keep = lo8 ? b[i] : b[i + 2];
-        const float send = lo8 ? b[i + 2] : b[i];
-        c[i] = keep + dpp<0x140>(send);
-    }
-    const bool lo4 = (lane & 4) == 0;      // partner lane j <-> 7-j inside 8 lanes
-    const float keep = lo4 ? c[0] : c[1];
-    const float send = lo4 ? c[1] : c[0];
-    float d = keep + dpp<0x141>(send);
-    d += dpp<0xB1>(d);                     // quad: lanes 4q..4q+3 hold the same row
-    d += dpp<0x4E>(d);
-    return d;
-}
 
 // HB > 0: x is the raw fp16 activation and the workgroup applies the block
 // Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
@@ -364,25 +282,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 }
 
 // ---- host side ---------------------------------------------------------------
-
-static int lut_slices(int64_t n_gt, int k) { return (int)(((int64_t)k * n_gt + LUT_SLOTS - 1) / LUT_SLOTS); }
-
-// Row tiles per workgroup for each linear: the grid aims at one workgroup per
-// CU, shared among the linears in proportion to their rows; a workgroup holds
-// at most LUT_WAVES * tiles_per_wave tiles.
-static void lut_plan(const int64_t* n_rt, int n, int slices, int tiles_per_wave, int* tpb, int* blocks) {
-    int64_t total = 0;
-    for (int i = 0; i < n; ++i) total += n_rt[i];
-    for (int i = 0; i < n; ++i) {
-        int64_t rb = total > 0 ? (LUT_CUS / slices) * n_rt[i] / total : 1;
-        if (rb < 1) rb = 1;
-        if (rb > n_rt[i]) rb = n_rt[i];
-        int64_t t = (n_rt[i] + rb - 1) / rb;
-        if (t > LUT_WAVES * tiles_per_wave) t = LUT_WAVES * tiles_per_wave;
-        tpb[i] = (int)t;
-        blocks[i] = (int)((n_rt[i] + t - 1) / t);
-    }
-}
 
 static size_t acc_bytes(int64_t d_out) { return ((size_t)d_out * 8 + 255) / 256 * 256; }
 

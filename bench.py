@@ -39,17 +39,25 @@ N_COPIES = 64
 CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 and 4096 x 14336)
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
-# only for the kernel source they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30690154
-TRAFFIC_K4_SOURCE_SHA256_PREFIX = "b13dcc340405bec4"
+# only for the kernel sources they were taken on: the summary under profiles/ gives the commands.
+TRAFFIC_K4_BYTES = 30690457
+TRAFFIC_K4_SOURCE_SHA256_PREFIX = "5b777bc180a6fe29"
+# the batch-1 GEMV kernel's source and the headers it includes
+HEADLINE_SOURCES = ("gemv_lut.hip", "lut_device.h", "fixed_sum.h", "fwht_device.h", "aqd_internal.h")
+
+
+def headline_source_digest() -> str:
+    """SHA-256 over the batch-1 GEMV kernel's source files, concatenated in HEADLINE_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in HEADLINE_SOURCES:
+        with open(os.path.join(ROOT, "additive_codebook_gemv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():
-    import hashlib
-    src = os.path.join(ROOT, "additive_codebook_gemv_amd", "csrc", "gemv_lut.hip")
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return TRAFFIC_K4_BYTES if digest.startswith(TRAFFIC_K4_SOURCE_SHA256_PREFIX) else None
+    return TRAFFIC_K4_BYTES if headline_source_digest().startswith(TRAFFIC_K4_SOURCE_SHA256_PREFIX) else None
 
 
 def algorithmic_bytes(k: int, d_out: int = D_OUT, d_in: int = D_IN, batch: int = BATCH) -> int:

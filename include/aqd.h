@@ -171,9 +171,13 @@ aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, 
  *               needed serves any number of calls, at any batch, on one
  *               stream.  Calls that may overlap in time need separate
  *               workspaces.
- * Batch 2..8 with batch * k > 4 runs on the matrix cores (the fp16 operand
- * mode of aqd_gemm_small_batch, result rounded to fp16); the other cases use
- * codeword lookups with v_dot2 accumulation.
+ * Batch 1 and 2 read per-group tables of codeword-activation products (one
+ * table per column, built on the matrix cores): one table lookup per code byte
+ * and column.  Batch 3..8 with batch * k > 4 runs on the matrix cores (the
+ * fp16 operand mode of aqd_gemm_small_batch, result rounded to fp16); the other
+ * cases use codeword lookups with v_dot2 accumulation.  (Inputs too long for the
+ * tables, k * ceil(d_in / 512) above 1020 at batch 1 or 510 at batch 2, take
+ * the latter routes too.)
  * Accumulation is fp32; the summation order is not specified, but it is fixed:
  * repeating a call on the same inputs gives the same bits.
  * packed_codes, x_rot and workspace 16-byte aligned; codebooks 16-byte aligned.

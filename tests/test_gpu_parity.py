@@ -192,10 +192,11 @@ def test_gemv_stack_sampled(orc):
 
 
 @pytest.mark.parametrize("d_out,d_in,M,batches", [
-    (1000, 1000, 3, (1, 3, 8)),       # ragged rows (not a multiple of 16) and groups (not a multiple of 64)
+    (1000, 1000, 3, (1, 2, 3, 8)),    # ragged rows (not a multiple of 16) and groups (not a multiple of 64)
     (1, 8, 1, (1, 2)),                # one row, one group
-    (33, 4096, 8, (1, 5)),            # M = 8 codebooks, every k
+    (33, 4096, 8, (1, 2, 5)),         # M = 8 codebooks, every k
     (2048, 512, 2, (7,)),
+    (16, 65536, 4, (1, 2)),           # at k = 4 too long for the batch-2 tables (k * d_in / 512 > 510)
 ])
 def test_gemv_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(21, extra=d_out * 7 + d_in + M)
@@ -229,7 +230,7 @@ def test_gemv_dyadic_bit_exact(orc, d_out, d_in, M):
     for k in range(1, M + 1):
         ref = orc.linear(codes, cb, s, k, x)
         assert np.max(np.abs(ref)) < 512          # every value and partial sum is exact in fp16/fp32
-        for B in (1, 8):
+        for B in (1, 2, 8):
             y = aqd.aqd_gemv(packed, cbdev, sdev, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()
             assert np.array_equal(y.astype(np.float64), ref[:B]), (k, B)
 
@@ -369,6 +370,17 @@ def test_gemv_workspace_reusable_and_deterministic(orc):
     y1 = aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, xr, lin.d_out, lin.d_in, 4, workspace=ws8)
     assert torch.equal(y1, outs[0])
     assert torch.equal(aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, x8, lin.d_out, lin.d_in, 4, workspace=ws8), y8)
+    # batch 2 (lookup tables of two columns) shares the zeroed region: it leaves it zero, repeats its bits,
+    # and batch 1 after it is unchanged
+    y2 = [aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), k, x8[:2].contiguous(), lin.d_out, lin.d_in, 4, workspace=ws8)
+          for k in (3, 3)]
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws8[:need]).item() == 0
+    assert torch.equal(y2[0], y2[1])
+    ref2 = orc.linear(codes, cb, s, 3, x8[:2].cpu().numpy())
+    assert normwise(y2[0].cpu().numpy(), ref2) <= TOL
+    assert torch.equal(aqd.aqd_gemv(packed, to_dev(cb), to_dev(s), 4, xr, lin.d_out, lin.d_in, 4, workspace=ws8),
+                       outs[0])
 
 
 def test_graph_replay_matches_eager(orc):
