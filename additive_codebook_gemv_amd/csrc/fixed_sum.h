@@ -17,13 +17,24 @@ namespace aqd {
 constexpr int FIX_FRAC = 24;
 constexpr int FIX_COUNT_SHIFT = 56;
 constexpr unsigned long long FIX_BIAS = 1ull << 47;
-constexpr double FIX_LIMIT = (double)((1ll << 47) - 1);
 constexpr int FIX_MAX_TERMS = 255;
 
+// The biased term of v: round-to-nearest-even(v * 2^24), saturated at
+// +-(2^47 - 1), plus 2^47.  Computed in fp32 and 32-bit integers without
+// rounding error: a = |v| * 2^24 is exact in fp32; its high word
+// h = floor(a * 2^-32) and the remainder a - h * 2^32 (a multiple of the ulp
+// of a below 2^32, so exact in fp32) are integers below 2^32 except for the
+// fraction bits of a < 2^24, which rintf rounds; round-to-nearest-even is
+// symmetric, so the sign is applied to the rounded magnitude.
 __device__ __forceinline__ unsigned long long fix_term(float v) {
-    double d = (double)v * (double)(1 << FIX_FRAC);
-    d = d > FIX_LIMIT ? FIX_LIMIT : (d < -FIX_LIMIT ? -FIX_LIMIT : d);
-    return (unsigned long long)(__double2ll_rn(d) + (long long)FIX_BIAS);
+    const float a = __builtin_fabsf(v) * (float)(1 << FIX_FRAC);
+    unsigned long long n = FIX_BIAS - 1;                         // saturated magnitude
+    if (a < (float)FIX_BIAS) {
+        const float h = __builtin_floorf(a * (1.0f / 4294967296.0f));
+        const float r = __builtin_fmaf(h, -4294967296.0f, a);
+        n = ((unsigned long long)(uint32_t)h << 32) + (uint32_t)__builtin_rintf(r);
+    }
+    return v < 0.f ? FIX_BIAS - n : FIX_BIAS + n;
 }
 
 // The word to add for term v.

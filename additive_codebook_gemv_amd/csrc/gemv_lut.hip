@@ -229,6 +229,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 #pragma unroll
     for (int s = 0; s < LUT_SLOTS; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
     const half2_t ones = half2_t{(_Float16)1.0f, (_Float16)1.0f};
+    const float one = opaque_one();
 
     // returned accumulator words are examined only after the last tile, so the
     // atomics' round trips overlap the remaining lookups
@@ -256,9 +257,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
                 const uint32_t w1 = (r >> 2) == 0 ? c1.x : (r >> 2) == 1 ? c1.y : (r >> 2) == 2 ? c1.z : c1.w;
                 const uint32_t a0 = lut_addr(w0, base[2 * pr], r & 3);
                 const uint32_t a1 = lut_addr(w1, base[2 * pr + 1], r & 3);
-                const half2_t v = half2_t{*reinterpret_cast<const _Float16*>(lds + a0),
-                                          *reinterpret_cast<const _Float16*>(lds + a1)};
-                a = pr == 0 ? __builtin_amdgcn_fdot2(v, ones, 0.0f, false) : __builtin_amdgcn_fdot2(v, ones, a, false);
+                const _Float16 e0 = *reinterpret_cast<const _Float16*>(lds + a0);
+                const _Float16 e1 = *reinterpret_cast<const _Float16*>(lds + a1);
+                // the first pair as one mixed-precision fma (fp16 inputs, fp32 sum), the others
+                // packed into one v_dot2 each
+                a = pr == 0 ? __builtin_fmaf((float)e0, one, (float)e1)
+                            : __builtin_amdgcn_fdot2(half2_t{e0, e1}, ones, a, false);
             }
             rows[r] = a;
         }

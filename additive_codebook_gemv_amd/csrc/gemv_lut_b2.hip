@@ -17,12 +17,14 @@
 // matrix-core product (32 codewords x 8 elements times 8 elements x 32
 // groups), one product per column.
 //
-// Per code byte a lane spends one address, one LDS read and, per pair of
-// slots, one pack and one v_dot2 per column: 3 VALU operations against 2 at
-// batch 1, for twice the output.  Row sums of both columns leave through the
-// counted fixed-point words of batch 1 (one word per column and row): lanes
-// 4q and 4q+1 hold row q's sums after the butterfly and add column 0 and
-// column 1 respectively, so one atomic instruction serves both columns.
+// Per code byte a lane spends one address and one LDS read, and per pair of
+// slots one mixed-precision fma per column (v_fma_mix_f32 adds the two fp16
+// entries of a column in fp32, picking the dword half by op_sel): 2 VALU
+// operations per code byte, as at batch 1, for twice the output.  Row sums of
+// both columns leave through the counted fixed-point words of batch 1 (one
+// word per column and row): lanes 4q and 4q+1 hold row q's sums after the
+// butterfly and add column 0 and column 1 respectively, so one atomic
+// instruction serves both columns.
 #include "lut_device.h"
 
 namespace aqd {
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
     uint32_t base[LUT2_SLOTS];
 #pragma unroll
     for (int s = 0; s < LUT2_SLOTS; ++s) base[s] = (uint32_t)(lane * 4) | ((uint32_t)s << 16);
-    const half2_t ones = half2_t{(_Float16)1.0f, (_Float16)1.0f};
+    const float one = opaque_one();
     const int col = lane & 1;                   // the column this lane adds after the butterfly
 
     unsigned long long old_word[TPW], term[TPW];
@@ -159,8 +161,8 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
             const uint32_t w1 = (r >> 2) == 0 ? c1.x : (r >> 2) == 1 ? c1.y : (r >> 2) == 2 ? c1.z : c1.w;
             const half2_t v0 = *reinterpret_cast<const half2_t*>(lds + lut_addr(w0, base[0], r & 3));
             const half2_t v1 = *reinterpret_cast<const half2_t*>(lds + lut_addr(w1, base[1], r & 3));
-            r0[r] = __builtin_amdgcn_fdot2(half2_t{v0.x, v1.x}, ones, 0.0f, false);
-            r1[r] = __builtin_amdgcn_fdot2(half2_t{v0.y, v1.y}, ones, 0.0f, false);
+            r0[r] = __builtin_fmaf((float)v0.x, one, (float)v1.x);      // v_fma_mix_f32, fp16 halves in
+            r1[r] = __builtin_fmaf((float)v0.y, one, (float)v1.y);
         }
         const float s0 = fold_rows(r0, lane);
         const float s1 = fold_rows(r1, lane);

@@ -90,6 +90,15 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
     return d;
 }
 
+// 1.0f in a scalar register the compiler cannot see through, so that
+// fma((float)h0, one, (float)h1) of two fp16 values stays one v_fma_mix_f32
+// instead of two conversions and an add.
+__device__ __forceinline__ float opaque_one() {
+    float v;
+    asm volatile("s_mov_b32 %0, 1.0" : "=s"(v));
+    return v;
+}
+
 // Row tiles per workgroup for each linear: the grid aims at one workgroup per
 // CU, shared among the linears in proportion to their rows; a workgroup holds
 // at most LUT_WAVES * tiles_per_wave tiles.
