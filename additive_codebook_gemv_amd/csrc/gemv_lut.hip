@@ -356,13 +356,14 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
     if (m == 0) return hipSuccess;
     a.n_lin = m;
     // two row tiles per wave, or four when two would need more workgroups than CUs (a second round)
+    const bool round4 = m == 1 && rotate_block == 0;   // the plain single-linear GEMV
     int tpw = LUT_TILES_PER_WAVE;
-    lut_plan(n_rt, m, a.slices, tpw, tpb, blocks);
+    lut_plan(n_rt, m, a.slices, tpw, tpb, blocks, round4);
     int64_t wgs = 0;
     for (int i = 0; i < m; ++i) wgs += (int64_t)a.slices * blocks[i];
     if (wgs > LUT_CUS) {
         tpw = LUT_TILES_PER_WAVE_BIG;
-        lut_plan(n_rt, m, a.slices, tpw, tpb, blocks);
+        lut_plan(n_rt, m, a.slices, tpw, tpb, blocks, round4);
     }
     uint8_t* acc = static_cast<uint8_t*>(ws);
     int wg = 0;
