@@ -125,12 +125,8 @@ __device__ __forceinline__ uint16_t f2h(float f) {  // round to nearest even
 __device__ __forceinline__ float bf2f(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }
-__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even, NaN kept quiet
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
+// float -> bf16, round to nearest even: gfx950's v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ void store_partial(float* part, int64_t d_out, int batch, unsigned split, int col,
                                               int64_t row0, float4 v) {

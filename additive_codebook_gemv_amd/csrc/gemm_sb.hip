@@ -54,14 +54,17 @@ struct XPlanes {
 __device__ __forceinline__ half2_t h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t u32(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
-// fp16 pair -> bf16 hi pair and bf16 lo pair (hi + lo equals the pair to 2^-16)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp16 pair -> bf16 hi pair and bf16 lo pair (hi + lo equals the pair to 2^-16).
+// Each pair conversion is one v_cvt_pk_bf16_f32 (round to nearest even).
 __device__ __forceinline__ void split_bf16(uint32_t h, uint32_t& hi, uint32_t& lo) {
     const half2_t v = h2(h);
     const float a = (float)v[0], b = (float)v[1];
-    const uint32_t ha = f2bf(a), hb = f2bf(b);
-    const uint32_t la = f2bf(a - bf2f((uint16_t)ha)), lb = f2bf(b - bf2f((uint16_t)hb));
-    hi = ha | (hb << 16);
-    lo = la | (lb << 16);
+    const bf16x2_t hv = bf16x2_t{(__bf16)a, (__bf16)b};
+    const bf16x2_t lv = bf16x2_t{(__bf16)(a - (float)hv[0]), (__bf16)(b - (float)hv[1])};
+    hi = __builtin_bit_cast(uint32_t, hv);
+    lo = __builtin_bit_cast(uint32_t, lv);
 }
 
 template <int NT, int MODE, int K>
