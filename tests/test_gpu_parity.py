@@ -197,6 +197,7 @@ def test_gemv_stack_sampled(orc):
     (33, 4096, 8, (1, 2, 5)),         # M = 8 codebooks, every k
     (2048, 512, 2, (7,)),
     (16, 65536, 4, (1, 2)),           # at k = 4 too long for the batch-2 tables (k * d_in / 512 > 510)
+    (16, 130560, 4, (1, 2)),          # 255 table slices, the most a row sum counts: batch 1 at k = 4, batch 2 at k = 2
 ])
 def test_gemv_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(21, extra=d_out * 7 + d_in + M)
