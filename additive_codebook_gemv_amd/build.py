@@ -23,6 +23,9 @@ FLAGS = [
     # keep the compiler from forming packed fp32 vector ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # kernel-argument preloading: the leading scalar arguments of a kernel arrive in SGPRs at launch,
+    # so its first loads need not wait for an argument load
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
 ]
 _NOISE = ("packed-fp32-ops' is not a recognized feature",)
 

@@ -73,7 +73,7 @@ struct LutLinearRef {
     uint16_t* y;
     int64_t d_out;
 };
-bool gemv_lut_grouped_supported(int64_t G, int k);
+bool gemv_lut_grouped_supported(int64_t G, int k, const int64_t* d_out, int n);
 size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n);
 // rotate_block 0: x is already rotated; 64/128/256: x is raw and each workgroup rotates what it needs
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,

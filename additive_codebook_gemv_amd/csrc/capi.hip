@@ -241,8 +241,10 @@ static aqd_status gemv_grouped(const aqd_linear* linears, int32_t n_linears, int
         }
         return AQD_OK;
     }
-    if (!gemv_lut_grouped_supported(d_in / 8, k))
-        return fail(AQD_ERR_UNSUPPORTED, "input too wide for one grouped launch");
+    int64_t d_outs[AQD_MAX_GROUP];
+    for (int i = 0; i < n_linears; ++i) d_outs[i] = linears[i].d_out;
+    if (!gemv_lut_grouped_supported(d_in / 8, k, d_outs, n_linears))
+        return fail(AQD_ERR_UNSUPPORTED, "input too wide or a linear with too many rows for one grouped launch");
     LutLinearRef refs[AQD_MAX_GROUP];
     for (int i = 0; i < n_linears; ++i)
         refs[i] = LutLinearRef{linears[i].packed_codes, linears[i].codebooks, linears[i].scales, linears[i].y,

@@ -64,8 +64,19 @@ struct LutArgs {
 // Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
 // butterflies and rounding of the standalone rotation (same bits), after the
 // optional sign flips of the randomized variant.
+//
+// The fields the first loads depend on come first, as scalars, so that the
+// launch preloads them into SGPRs (kernel-argument preloading; a by-value
+// struct cannot be preloaded): a workgroup then issues its table operand and
+// code loads without first waiting for an argument load.  packed0, codebooks0,
+// plane_bytes0, n_rt0 and tpb0 are those of linear 0, which a single-linear
+// launch uses; the other fields stay in the struct.
 template <int WAVES, int K, bool MULTI, int HB, int TPW>
-__global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
+__global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __restrict__ packed0,
+                                                              const uint16_t* __restrict__ codebooks0,
+                                                              const uint16_t* __restrict__ xin, int64_t plane_bytes0,
+                                                              int n_rt0, int G, int slices, int n_slots, int tpb0,
+                                                              LutArgs p) {
     constexpr int XS_BYTES = HB > 0 ? LUT_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
     __shared__ __align__(16) uint8_t lds[LUT_BYTES + XS_BYTES + 16];
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds + LUT_BYTES);              // [slot][512]
@@ -81,11 +92,16 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
             if (i < p.n_lin && (int)blockIdx.x >= p.lin[i].wg_begin) l = i;
     }
     const LutLinear L = p.lin[MULTI ? l : 0];
-    const int local = (int)blockIdx.x - L.wg_begin;
-    const int slice = local % p.slices;
-    const int rb = local / p.slices;
-    const int64_t t0 = (int64_t)rb * L.tiles_per_block;
-    const int64_t t1 = t0 + L.tiles_per_block < L.n_rt ? t0 + L.tiles_per_block : L.n_rt;
+    const uint8_t* const packed = MULTI ? L.packed : packed0;
+    const uint16_t* const codebooks = MULTI ? L.codebooks : codebooks0;
+    const int64_t plane_bytes = MULTI ? L.plane_bytes : plane_bytes0;
+    const int64_t n_rt = MULTI ? L.n_rt : (int64_t)n_rt0;
+    const int tiles_per_block = MULTI ? L.tiles_per_block : tpb0;
+    const int local = (int)blockIdx.x - (MULTI ? L.wg_begin : 0);
+    const int slice = local % slices;
+    const int rb = local / slices;
+    const int64_t t0 = (int64_t)rb * tiles_per_block;
+    const int64_t t1 = t0 + tiles_per_block < n_rt ? t0 + tiles_per_block : n_rt;
 
     // slot s of this slice: q = slice*4 + s -> group tile q / K, codebook q % K.
     // Every load below is unconditional (inactive slots, padding groups and
@@ -96,10 +112,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 #pragma unroll
     for (int s = 0; s < LUT_SLOTS; ++s) {
         const int q = slice * LUT_SLOTS + s;
-        slot_on[s] = q < p.n_slots;
+        slot_on[s] = q < n_slots;
         const int qq = slot_on[s] ? q : 0;
-        slot_buf[s] = slot_rsrc(L.packed + (int64_t)(qq % K) * L.plane_bytes + (int64_t)(qq / K) * L.n_rt * TILE_BYTES,
-                                L.n_rt * TILE_BYTES);
+        slot_buf[s] = slot_rsrc(packed + (int64_t)(qq % K) * plane_bytes + (int64_t)(qq / K) * n_rt * TILE_BYTES,
+                                n_rt * TILE_BYTES);
     }
 
     // ---- table operands first (loads complete in order)
@@ -113,14 +129,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int q = slice * LUT_SLOTS + 2 * pair + h;
-            const int qq = q < p.n_slots ? q : 0;
+            const int qq = q < n_slots ? q : 0;
             const int e0 = 4 * (lane >> 5);
             const int c = cb * 32 + (lane & 31);
             const int64_t g = (int64_t)(qq / K) * TILE_GROUPS + gb * 32 + (lane & 31);
-            bok[u][h] = q < p.n_slots && g < p.G;
-            const int64_t gc = g < p.G ? g : p.G - 1;
-            av[u][h] = *reinterpret_cast<const uint2*>(L.codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
-            if (HB == 0) bv[u][h] = *reinterpret_cast<const uint2*>(p.x + gc * GROUP + e0);
+            bok[u][h] = q < n_slots && g < G;
+            const int64_t gc = g < G ? g : G - 1;
+            av[u][h] = *reinterpret_cast<const uint2*>(codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
+            if (HB == 0) bv[u][h] = *reinterpret_cast<const uint2*>(xin + gc * GROUP + e0);
         }
     }
     // raw activation blocks for the rotation: slot s needs inputs 512*tile .. +512 (tile = q / K),
@@ -137,10 +153,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
             const int blk = wave + b * WAVES;
             const int sl = (blk < NBLK ? blk : 0) / BLK_PER_SLOT, j = (blk < NBLK ? blk : 0) % BLK_PER_SLOT;
             const int q = slice * LUT_SLOTS + sl;
-            const int64_t in0 = (int64_t)((q < p.n_slots ? q : 0) / K) * (TILE_GROUPS * GROUP) + (int64_t)j * HB;
-            xok[b] = blk < NBLK && q < p.n_slots && in0 < p.G * GROUP;
+            const int64_t in0 = (int64_t)((q < n_slots ? q : 0) / K) * (TILE_GROUPS * GROUP) + (int64_t)j * HB;
+            xok[b] = blk < NBLK && q < n_slots && in0 < (int64_t)G * GROUP;
 #pragma unroll
-            for (int e = 0; e < E; ++e) xv[b][e] = h2f(p.x[xok[b] ? in0 + e * 64 + lane : lane]);
+            for (int e = 0; e < E; ++e) xv[b][e] = h2f(xin[xok[b] ? in0 + e * 64 + lane : lane]);
             if (p.signs) {                                      // randomized rotation: eps = -1 where the bit is set
 #pragma unroll
                 for (int e = 0; e < E; ++e)
@@ -276,11 +292,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(LutArgs p) {
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        if (!mine[u] || !fix_is_last(old_word[u], p.slices)) continue;
+        if (!mine[u] || !fix_is_last(old_word[u], slices)) continue;
         // this lane added the last contribution of its row: it holds the complete sum
         const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
         if (row >= L.d_out) continue;
-        L.y[row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], p.slices));
+        L.y[row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], slices));
         __hip_atomic_store(L.acc + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -292,11 +308,14 @@ static size_t acc_bytes(int64_t d_out) { return ((size_t)d_out * 8 + 255) / 256 
 size_t gemv_lut_workspace_bytes(const Geometry& g) { return acc_bytes(g.d_out); }
 
 bool gemv_lut_supported(const Geometry& g, int batch, int k) {
-    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && lut_slices(g.n_gt, k) <= LUT_MAX_SLICES;
+    return batch == 1 && g.n_gt > 0 && g.n_rt > 0 && g.n_rt <= LUT_MAX_ROW_TILES &&
+           lut_slices(g.n_gt, k) <= LUT_MAX_SLICES;
 }
 
-bool gemv_lut_grouped_supported(int64_t G, int k) {
+bool gemv_lut_grouped_supported(int64_t G, int k, const int64_t* d_out, int n) {
     const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
+    for (int i = 0; i < n; ++i)
+        if ((d_out[i] + TILE_ROWS - 1) / TILE_ROWS > LUT_MAX_ROW_TILES) return false;
     return n_gt > 0 && lut_slices(n_gt, k) <= LUT_MAX_SLICES;
 }
 
@@ -309,14 +328,17 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
 template <bool MULTI, int HB, int TPW>
 static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
     switch (k) {
-        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
-        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB, TPW>), gd, bd, 0, s, a); break;
+#define AQD_LUT_ARGS a.lin[0].packed, a.lin[0].codebooks, a.x, a.lin[0].plane_bytes, (int)a.lin[0].n_rt, (int)a.G, \
+                     a.slices, a.n_slots, a.lin[0].tiles_per_block, a
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+#undef AQD_LUT_ARGS
     }
 }
 

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
 size_t gemv_lut2_workspace_bytes(const Geometry& g) { return ((size_t)g.d_out * 2 * 8 + 255) / 256 * 256; }
 
 bool gemv_lut2_supported(const Geometry& g, int batch, int k) {
-    return batch == 2 && g.n_gt > 0 && g.n_rt > 0 && lut_slices(g.n_gt, k, LUT2_SLOTS) <= LUT_MAX_SLICES;
+    return batch == 2 && g.n_gt > 0 && g.n_rt > 0 && g.n_rt <= LUT_MAX_ROW_TILES &&
+           lut_slices(g.n_gt, k, LUT2_SLOTS) <= LUT_MAX_SLICES;
 }
 
 template <int TPW>

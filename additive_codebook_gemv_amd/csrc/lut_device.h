@@ -126,6 +126,11 @@ static inline void lut_plan(const int64_t* n_rt, int n, int slices, int tiles_pe
     }
 }
 
+// Code tiles are addressed through buffer descriptors with 32-bit offsets (and
+// the tiles of one group tile of one plane are n_rt * 1 KiB long), so a layer
+// may have at most this many row tiles (about 33.5 million rows).
+constexpr int64_t LUT_MAX_ROW_TILES = 0x7FFFFFFF / TILE_BYTES;
+
 // Table slices of a launch: k * n_gt slots, LUT_SLOTS per workgroup.
 static inline int lut_slices(int64_t n_gt, int k, int slots_per_wg = LUT_SLOTS) {
     return (int)(((int64_t)k * n_gt + slots_per_wg - 1) / slots_per_wg);
