@@ -397,11 +397,15 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
         wg += a.slices * blocks[i];
     }
     const dim3 gd((unsigned)wg), bd(64 * LUT_WAVES);
-    if (rotate_block == 64) launch_tpw<true, 64>(tpw, k, gd, bd, s, a);
-    else if (rotate_block == 128) launch_tpw<true, 128>(tpw, k, gd, bd, s, a);
-    else if (rotate_block == 256) launch_tpw<true, 256>(tpw, k, gd, bd, s, a);
-    else if (m == 1) launch_tpw<false, 0>(tpw, k, gd, bd, s, a);
-    else launch_tpw<true, 0>(tpw, k, gd, bd, s, a);
+    // one linear: the instantiation that takes every field its first loads need from the preloaded
+    // leading arguments
+    const bool one = m == 1;
+    if (rotate_block == 64) one ? launch_tpw<false, 64>(tpw, k, gd, bd, s, a) : launch_tpw<true, 64>(tpw, k, gd, bd, s, a);
+    else if (rotate_block == 128)
+        one ? launch_tpw<false, 128>(tpw, k, gd, bd, s, a) : launch_tpw<true, 128>(tpw, k, gd, bd, s, a);
+    else if (rotate_block == 256)
+        one ? launch_tpw<false, 256>(tpw, k, gd, bd, s, a) : launch_tpw<true, 256>(tpw, k, gd, bd, s, a);
+    else one ? launch_tpw<false, 0>(tpw, k, gd, bd, s, a) : launch_tpw<true, 0>(tpw, k, gd, bd, s, a);
     return hipGetLastError();
 }
 
