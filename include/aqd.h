@@ -203,8 +203,8 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
  *            zero-filled before first use and left zeroed, as for aqd_gemv.
  * Errors as for aqd_gemv; AQD_ERR_SHAPE for n_linears outside 1..AQD_MAX_GROUP;
  * AQD_ERR_UNSUPPORTED (nothing launched) when k * ceil(d_in / 512) exceeds
- * 1020 or a linear has more than 33,554,416 rows (the one-launch lookup tables
- * cannot hold them; aqd_gemv per linear still can).
+ * 1020: the lookup tables of one launch cannot cover the input (aqd_gemv per
+ * linear still can).
  * ------------------------------------------------------------------------- */
 #define AQD_MAX_GROUP 4
 

@@ -211,6 +211,9 @@ def test_grouped_gemv_rejects_bad_arguments(L):
     assert L.aqd_gemv_grouped(big, 3, 2, FAKE, 4096, FAKE, need - 1, None) == E_WS
     assert L.aqd_gemv_grouped(lins(2), 2, 1, FAKE_ODD, 256, FAKE, 1 << 20, None) == E_ALIGN
     assert L.aqd_gemv_grouped_workspace_bytes(lins(5), 5, 256) == 0
+    # the limit of one launch's lookup tables, refused before anything is enqueued: more than 1020
+    # slots (k * ceil(d_in / 512))
+    assert L.aqd_gemv_grouped(lins(2, 64, 4), 2, 4, FAKE, 131072, FAKE, 1 << 20, None) == E_UNSUP
     # the fused rotation: block must be 64/128/256 and divide d_in
     assert L.aqd_rotate_gemv_grouped(lins(2), 2, 1, FAKE, 256, 32, FAKE, 1 << 20, None) == E_BLOCK
     assert L.aqd_rotate_gemv_grouped(lins(2), 2, 1, FAKE, 192, 128, FAKE, 1 << 20, None) == E_BLOCK
