@@ -658,6 +658,26 @@ def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
     assert e <= TOL, e
 
 
+def test_prefill_maximum_batch(orc):
+    """The largest batch the ABI accepts (AQD_PREFILL_MAX_BATCH columns) on a small layer: columns at the
+    ends of 128- and 256-column tiles and the last column against the oracle, and a bit-identical repeat."""
+    B, d_out, d_in, M, k = aqd.AQD_PREFILL_MAX_BATCH, 272, 1024, 2, 2
+    g = wl.rng(57)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    x = wl.gen_x(g, B, d_in, "f16")
+    cdev, cbdev, sdev = _layer_dev(codes, cb, s)
+    packed = aqd.aqd_pack_codes(cdev)
+    xd = to_dev(x)
+    y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, xd, d_out, d_in, M)
+    assert torch.equal(y, aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, xd, d_out, d_in, M))
+    extra = np.random.Generator(np.random.PCG64(58)).choice(B, size=6, replace=False)
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, B // 2, B - 257, B - 256, B - 1], extra]))
+    ref = orc.linear(codes, cb, s, k, x[cols])
+    e = normwise(y.cpu().numpy()[cols], ref)
+    record(test="prefill_max_batch", shape=[d_out, d_in], batch=B, k=k, err=e)
+    assert e <= TOL, e
+
+
 def test_prefill_empty_input_gives_zero():
     d_out = 40
     s = to_dev(np.ones(d_out, dtype=np.float16))
