@@ -247,7 +247,9 @@ def test_prefill_rejects_bad_arguments(L):
     assert need > 0                                # 16 row blocks x 4 column blocks: the inputs are split
     assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, None, 0, None) == E_WS
     assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, FAKE, need - 1, None) == E_WS
-    assert L.aqd_gemm_prefill_workspace_bytes(lay(d_out=14336, d_in=4096, M=4), 4096) == 0   # no split
+    tall = lay(d_out=14336, d_in=4096, M=4)
+    assert L.aqd_gemm_prefill_workspace_bytes(tall, 511) == 0                   # fused, no split
+    assert L.aqd_gemm_prefill_workspace_bytes(tall, 4096) == 14336 * 4096 * 2   # staged fp16 weights, no split
     assert L.aqd_gemm_prefill_workspace_bytes(big, 0) == 0
 
 

@@ -605,6 +605,10 @@ def test_small_batch_tiered_edge(orc):
     (512, 960, 4, (128,)),            # 15 chunks split one per workgroup: odd chunk counts per split
     (33, 8, 8, (3,)),                 # one group, M = 8, every k
     (600, 8192, 4, (520,)),           # 256-column tiles (batch >= 512, long inputs): ragged rows and columns
+    (40, 600, 3, (600,)),             # fp16 weights staged once (batch >= 512): ragged rows, groups, chunks,
+                                      # columns; one-chunk splits with the zero padding chunk
+    (33, 8, 8, (512,)),               # staged weights: one group (the rest of its tile zeroed), M = 8
+    (1000, 1000, 3, (513,)),          # staged weights: several row blocks, one column past two 256-column tiles
 ])
 def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(51, extra=d_out * 7 + d_in + M)
@@ -622,21 +626,24 @@ def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
 
 
 def test_prefill_dyadic_bit_exact(orc):
-    """Exact arithmetic: every split, chunk and column of the tiled product gives the oracle's bits."""
+    """Exact arithmetic: every split, chunk and column of the tiled product gives the oracle's bits, with
+    the weights rebuilt per workgroup (160 columns) and staged once as fp16 (600 columns)."""
     d_out, d_in, M = 300, 2048, 4
-    codes, cb, s, x = wl.dyadic_case(wl.rng(52), d_out, d_in, M, batch=160)
+    codes, cb, s, x = wl.dyadic_case(wl.rng(52), d_out, d_in, M, batch=600)
     cdev, cbdev, sdev = _layer_dev(codes, cb, s)
     packed = aqd.aqd_pack_codes(cdev)
     for k in (1, 4):
         ref = orc.linear(codes, cb, s, k, x)
-        y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(x), d_out, d_in, M).cpu().numpy()
-        assert np.array_equal(y.astype(np.float64), ref), k
+        for B in (160, 600):
+            y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()
+            assert np.array_equal(y.astype(np.float64), ref[:B]), (k, B)
 
 
 @pytest.mark.parametrize("d_out,d_in,batch,k", [
     (4096, 14336, 512, 4),      # down projection, 512 prompt tokens
     (4096, 14336, 512, 2),
     (14336, 4096, 1024, 4),     # gate / up projection, 1024 prompt tokens
+    (4096, 14336, 2048, 4),     # down projection, 2048 prompt tokens (fp16 weights staged once, split inputs)
 ])
 def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
     """Full 8B-shape layers in the launch configuration the benchmark times; eight sampled columns
