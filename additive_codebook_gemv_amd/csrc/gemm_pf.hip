@@ -254,13 +254,19 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
 // groups; a wave owns 64 rows (4 A fragments) x 128 columns (8 B fragments),
 // which reads fewer operand bytes from LDS per product than 32 x 256.
 
+#ifndef PFW_WAVES_CFG
+#define PFW_WAVES_CFG 8
+#endif
 constexpr int PFW_COLS = 256;                          // batch columns per workgroup
-constexpr int PFW_WAVE_FRAGS = 4;                      // A fragments per wave (64 rows)
-constexpr int PFW_WAVE_COLF = 8;                       // B fragments per wave (128 columns)
+constexpr int PFW_WAVES = PFW_WAVES_CFG;               // waves per workgroup
+constexpr int PFW_WC = 2;                              // column groups of waves (128 columns each)
+constexpr int PFW_WR = PFW_WAVES / PFW_WC;             // row groups of waves
+constexpr int PFW_WAVE_FRAGS = PF_TILES / PFW_WR;      // A fragments per wave
+constexpr int PFW_WAVE_COLF = PFW_COLS / 16 / PFW_WC;  // B fragments per wave (128 columns)
 constexpr int PFW_MIN_BATCH = 512;                     // below this the fused kernel is faster everywhere
 constexpr int64_t PFW_MAX_WEIGHT_BYTES = int64_t(1) << 31;   // largest fp16 weight kept in the workspace
 
-static_assert(PF_WAVES == 8 && PF_TILES == 16, "the two-phase tile assumes 8 waves over 16 row tiles");
+static_assert(PF_TILES == 16 && (PFW_WAVES == 4 || PFW_WAVES == 8), "two-phase tile: 16 row tiles, 4 or 8 waves");
 
 static int64_t pfw_weight_bytes(const Geometry& g) { return g.plane_bytes * 16; }
 
@@ -319,7 +325,7 @@ struct PfwArgs {
     int batch, chunks_per_split, direct;
 };
 
-__global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4) void gemm_pfw_kernel(PfwArgs p) {
+__global__ __launch_bounds__(64 * PFW_WAVES, PFW_WAVES / 4) void gemm_pfw_kernel(PfwArgs p) {
     constexpr int XB = PFW_COLS * PF_CHUNK * 2;                           // 256 columns x 128 B
     constexpr int AB = PF_TILES * 2 * 1024;                               // 16 tiles x 2 fragments
     __shared__ __align__(16) uint8_t x0[XB];
@@ -332,8 +338,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4) void gemm_pfw_kernel(P
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);              // uniform: scalar addresses
     const int r = lane & 15;
     const int kq = lane >> 4;
-    const int wr = wave & 3;                                               // row group: 4 row tiles
-    const int wc = wave >> 2;                                              // column group: 128 columns
+    const int wr = wave % PFW_WR;                                          // row group of the wave
+    const int wc = wave / PFW_WR;                                          // column group: 128 columns
     const int64_t rtb = (int64_t)blockIdx.x * PF_TILES;
     const int col0 = blockIdx.y * PFW_COLS;
     const int64_t c0 = (int64_t)blockIdx.z * p.chunks_per_split;
@@ -344,8 +350,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4) void gemm_pfw_kernel(P
     // padding chunk after the split gets zeros on both sides.
     auto stage = [&](int64_t ch, uint8_t* xd, uint8_t* ad) {
 #pragma unroll
-        for (int q = 0; q < PFW_COLS / 8 / PF_WAVES; ++q) {
-            const int blk = q * PF_WAVES + wave;
+        for (int q = 0; q < PFW_COLS / 8 / PFW_WAVES; ++q) {
+            const int blk = q * PFW_WAVES + wave;
             const int col = blk * 8 + (lane >> 3);
             const int piece = (lane & 7) ^ ((col >> 1) & 7);
             const int64_t kk = ch * PF_CHUNK + piece * GROUP;
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4) void gemm_pfw_kernel(P
         const int64_t jt = chc / (TILE_GROUPS / PF_CHUNK_GROUPS);
         const int g0 = (int)(chc % (TILE_GROUPS / PF_CHUNK_GROUPS)) * PF_CHUNK_GROUPS;
 #pragma unroll
-        for (int q = 0; q < 2 * PF_TILES / PF_WAVES; ++q) {
-            const int idx = q * PF_WAVES + wave;
+        for (int q = 0; q < 2 * PF_TILES / PFW_WAVES; ++q) {
+            const int idx = q * PFW_WAVES + wave;
             const int f = idx >> 1;
             const int h = idx & 1;
             uint8_t* dst = ad + idx * 1024;
@@ -563,7 +569,7 @@ static hipError_t launch_gemm_pfw(const uint8_t* packed, const uint16_t* codeboo
     a.batch = batch;
     a.chunks_per_split = pl.chunks_per_split;
     hipLaunchKernelGGL(gemm_pfw_kernel, dim3((unsigned)pl.row_blocks, (unsigned)pl.col_blocks, (unsigned)pl.splits),
-                       dim3(64 * PF_WAVES), 0, s, a);
+                       dim3(64 * PFW_WAVES), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess || a.direct) return e;
     return launch_split_reduce(static_cast<const float*>(ws), scales, y, g.d_out, batch, pl.splits, s);

@@ -305,20 +305,27 @@ aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* cod
  *
  *     y[n][i] = s_i * sum_c W_k[i][c] * x_rot[n][c]      (fp32 out)
  *
- * Each workgroup rebuilds 256 weight rows as fp16 codeword sums (packed fp16
- * adds, as the fp16 small-batch mode) and multiplies them by 128 activation
- * columns with v_mfma_f32_16x16x32_f16, accumulating in fp32.  Throughput is
- * meant for batch >= 128; any batch in range is correct.
+ * The weights are fp16 codeword sums (packed fp16 adds in plane order, as the
+ * fp16 small-batch mode), multiplied with v_mfma_f32_16x16x32_f16 and
+ * accumulated in fp32.  Each workgroup rebuilds its 256 weight rows from the
+ * codes up to batch 511, and for d_in >= 8192 also at k <= 2 (any batch) and
+ * k = 3, 4 (batch up to 1023).  Otherwise the library first writes the whole
+ * fp16 weight (2 * d_out * d_in bytes) into the workspace and the product
+ * reads it from there.  Both forms use the same fp16 weights.  Throughput is meant for batch >= 128; any batch
+ * in range is correct.
  *
  * packed_codes, codebooks, scales: as for aqd_gemv; only the first k planes
  *               and codebooks are read.
  * x_rot:        fp16 [batch][d_in], the rotated activation, 16-byte aligned.
  * y:            fp32 [batch][d_out], 4-byte aligned.
  * k:            1..M.  batch: 1..AQD_PREFILL_MAX_BATCH.
- * workspace:    aqd_gemm_prefill_workspace_bytes(layer, batch) bytes (0 when
- *               the tiles fill the chip without splitting the inputs; NULL is
- *               then allowed), 16-byte aligned, fully overwritten by every
- *               call; calls that may overlap in time need separate ones.
+ * workspace:    aqd_gemm_prefill_workspace_bytes(layer, batch) bytes, the
+ *               largest over k: the fp16 weight where it is staged (layers up
+ *               to 2 GiB of fp16 weights; larger ones always rebuild in the
+ *               workgroups) plus fp32 partial sums when the inputs are split.
+ *               0 when neither is needed (NULL is then allowed).  16-byte
+ *               aligned, fully overwritten by every call; calls that may
+ *               overlap in time need separate ones.
  * The summation order is fixed (input splits are added in order by a second
  * kernel), so repeating a call gives the same bits.
  * Errors: AQD_ERR_SHAPE for batch out of range, otherwise as for
