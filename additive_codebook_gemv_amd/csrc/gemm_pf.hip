@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);              // uniform: scalar addresses
     const int r = lane & 15;      // A: row in the fragment; B: column in the fragment
     const int kq = lane >> 4;     // 8-input slot inside a 32-input MFMA step
     const int64_t rtb = (int64_t)blockIdx.x * PF_TILES;                    // first row tile of the workgroup
