@@ -40,7 +40,7 @@ CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 an
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
 # only for the kernel sources they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30682220
+TRAFFIC_K4_BYTES = 30683787
 TRAFFIC_K4_SOURCE_SHA256_PREFIX = "6828fdc5a6043ece"
 # the batch-1 GEMV kernel's source and the headers it includes
 HEADLINE_SOURCES = ("gemv_lut.hip", "lut_device.h", "fixed_sum.h", "fwht_device.h", "aqd_internal.h")
@@ -404,7 +404,8 @@ def measure_encode(aqd, wl, torch, dev, reps: int = 3):
 
 
 def measure_prefill(aqd, wl, torch, dev, reps: int = 5):
-    """Prefill (batch 128 / 512 / 2048 prompt tokens) through the fused dequantize + matrix-core kernel on
+    """Prefill (batch 128 / 512 / 2048 prompt tokens) through aqd_gemm_prefill (weights rebuilt per workgroup,
+    or staged once as fp16 at the larger batches, then the matrix cores) on
     the 4096x14336 and 14336x4096 shapes, k = 2 and 4.  Beside each, the dense fp16 GEMM of the same shape
     through torch.matmul (the vendor GEMM library) on an uncompressed weight, as a reference point for what
     the matrix cores deliver on a plain GEMM here.  At these sizes the work is compute-bound, so no cold
