@@ -229,6 +229,30 @@ def test_grouped_gemv_rejects_bad_arguments(L):
     assert L.aqd_rotate_gemv_grouped_signed(lins(2), 2, 3, FAKE, 256, 64, sg, FAKE, 1 << 20, None) == E_K
 
 
+def test_prefill_workspace_follows_the_plan(L):
+    """The prefill workspace is the staged fp16 weight (2 bytes per weight, tile padding included) plus,
+    when the inputs are split, one float4 per (split, column, row quad); the plan charges the reduce
+    of the partials, so tall layers split at most in two.  Host logic only: nothing is launched."""
+    def pf(d_out, d_in, batch):
+        return L.aqd_gemm_prefill_workspace_bytes(lay(d_out=d_out, d_in=d_in, M=4), batch)
+
+    def partials(d_out, batch, splits):
+        return splits * batch * ((d_out + 3) // 4) * 16
+    w = 4096 * 14336 * 2                        # the staged weight of either 8B MLP shape
+    # 4096x14336: 16 row blocks x 8 column blocks fill half the chip; two splits, staged at k = 3, 4
+    assert pf(4096, 14336, 2048) == partials(4096, 2048, 2) + w
+    # 14336x4096 at 512 columns: 112 tiles; two splits (sixteen would read 470 MB of partials back)
+    assert pf(14336, 4096, 512) == partials(14336, 512, 2) + w
+    # 14336x4096 at 1024 and 2048 columns: the tiles cover the chip, no split
+    assert pf(14336, 4096, 1024) == w
+    assert pf(14336, 4096, 2048) == w
+    # below 512 columns nothing is staged; 511 columns of 14336x4096 need no split either
+    assert pf(14336, 4096, 511) == 0
+    # a layer of more than 2 GiB of fp16 weight is never staged: partials only, or nothing
+    big = pf(65536, 32768, 4096)
+    assert big < 65536 * 32768 * 2 and big % 16 == 0
+
+
 def test_prefill_rejects_bad_arguments(L):
     def pf(packed=FAKE, cb=FAKE, s=FAKE, k=1, x=FAKE, y=FAKE, batch=256, layer=None, ws=FAKE, nws=1 << 30):
         return L.aqd_gemm_prefill(packed, cb, s, k, x, y, batch, layer if layer is not None else lay(), ws, nws,
