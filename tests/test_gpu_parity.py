@@ -644,6 +644,11 @@ def test_prefill_dyadic_bit_exact(orc):
     (4096, 14336, 512, 2),
     (14336, 4096, 1024, 4),     # gate / up projection, 1024 prompt tokens
     (4096, 14336, 2048, 4),     # down projection, 2048 prompt tokens (fp16 weights staged once, split inputs)
+    (4096, 14336, 2048, 2),     # rebuilt per workgroup, 256-column tiles, split inputs
+    (4096, 14336, 128, 4),      # rebuilt per workgroup, 128-column tiles, split inputs
+    (14336, 4096, 128, 2),
+    (14336, 4096, 512, 4),      # staged weights, two splits
+    (14336, 4096, 2048, 2),     # staged weights, two rounds of workgroups
 ])
 def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
     """Full 8B-shape layers in the launch configuration the benchmark times; eight sampled columns
