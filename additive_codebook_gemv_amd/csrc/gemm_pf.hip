@@ -236,8 +236,8 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
 // Two-phase form for large batches.  The fused kernel above rebuilds every
 // weight group once per column block, with k random codeword reads from LDS
 // that conflict in the bank groups; at a few column blocks and more that
-// rebuild, not the products, sets the time.  Here the weights are rebuilt once
-// per call instead:
+// rebuild is a large share of its time.  Here the weights are rebuilt once per
+// call instead:
 //   1. pf_dequant_kernel writes W_k as fp16 into the workspace, in the order
 //      of the packed codes with each code byte widened to the 16 bytes (8
 //      halves) of its group's codeword sum.  The sum is the same packed fp16
@@ -252,13 +252,12 @@ __global__ __launch_bounds__(64 * PF_WAVES, PF_WAVES / 4 * PF_PER_CU) void gemm_
 //      one conflict-free 16-byte read.
 // Workgroup tile: 256 rows x 256 columns, 8 waves as 4 row groups x 2 column
 // groups; a wave owns 64 rows (4 A fragments) x 128 columns (8 B fragments),
-// which reads fewer operand bytes from LDS per product than 32 x 256.
+// which reads fewer operand bytes from LDS per product than 32 x 256.  (4 waves
+// of 128 x 128 would read fewer still, but with 256 accumulators per wave the
+// compiler moves them between register ranges every step and spills.)
 
-#ifndef PFW_WAVES_CFG
-#define PFW_WAVES_CFG 8
-#endif
 constexpr int PFW_COLS = 256;                          // batch columns per workgroup
-constexpr int PFW_WAVES = PFW_WAVES_CFG;               // waves per workgroup
+constexpr int PFW_WAVES = 8;                           // waves per workgroup
 constexpr int PFW_WC = 2;                              // column groups of waves (128 columns each)
 constexpr int PFW_WR = PFW_WAVES / PFW_WC;             // row groups of waves
 constexpr int PFW_WAVE_FRAGS = PF_TILES / PFW_WR;      // A fragments per wave
@@ -266,7 +265,7 @@ constexpr int PFW_WAVE_COLF = PFW_COLS / 16 / PFW_WC;  // B fragments per wave (
 constexpr int PFW_MIN_BATCH = 512;                     // below this the fused kernel is faster everywhere
 constexpr int64_t PFW_MAX_WEIGHT_BYTES = int64_t(1) << 31;   // largest fp16 weight kept in the workspace
 
-static_assert(PF_TILES == 16 && (PFW_WAVES == 4 || PFW_WAVES == 8), "two-phase tile: 16 row tiles, 4 or 8 waves");
+static_assert(PF_TILES == 16 && PFW_WAVE_FRAGS == 4 && PFW_WAVE_COLF == 8, "two-phase tile: 64 x 128 per wave");
 
 static int64_t pfw_weight_bytes(const Geometry& g) { return g.plane_bytes * 16; }
 
