@@ -271,8 +271,9 @@ static int64_t pfw_weight_bytes(const Geometry& g) { return g.plane_bytes * 16; 
 
 static int pf_nb(const Geometry& g, int batch, int k);
 
-// The fused kernel stays where it measured faster: its 256-column form (long inputs) with few
-// codebooks, whose rebuild is cheap, or below 1024 columns.
+// The fused kernel stays where it measured faster or equal: its 256-column form at k <= 2, and at
+// k = 3, 4 below 1024 columns.  The staged form takes k = 3, 4 from 1024 columns and k >= 5 (the
+// fused kernel's 128-column form) from 512.
 static bool pfw_used(const Geometry& g, int batch, int k) {
     if (batch < PFW_MIN_BATCH || g.plane_bytes == 0 || pfw_weight_bytes(g) > PFW_MAX_WEIGHT_BYTES) return false;
     return pf_nb(g, batch, k) == 8 || (k >= 3 && batch >= 1024);
@@ -440,11 +441,11 @@ __global__ __launch_bounds__(64 * PFW_WAVES, PFW_WAVES / 4) void gemm_pfw_kernel
 }
 
 // B fragments per wave (16 batch columns each).  128 columns by default; 256 where
-// they measured faster (batch >= 512 over a long input dimension, k <= 4: more
-// codebooks would spill), which doubles the accumulators and halves the
-// codeword gathers per product.
+// they measured faster (k <= 4: more codebooks would spill; batch >= 512, or
+// >= 256 over a short input dimension, whose split reduce is small), which
+// doubles the accumulators and halves the codeword gathers per product.
 static int pf_nb(const Geometry& g, int batch, int k) {
-    return batch >= 512 && g.d_in >= 8192 && k <= 4 ? 16 : 8;
+    return k <= 4 && (batch >= 512 || (batch >= 256 && g.d_in < 8192)) ? 16 : 8;
 }
 
 struct PfPlan {

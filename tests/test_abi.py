@@ -241,13 +241,17 @@ def test_prefill_workspace_follows_the_plan(L):
     w = 4096 * 14336 * 2                        # the staged weight of either 8B MLP shape
     # 4096x14336: 16 row blocks x 8 column blocks fill half the chip; two splits, staged at k = 3, 4
     assert pf(4096, 14336, 2048) == partials(4096, 2048, 2) + w
-    # 14336x4096 at 512 columns: 112 tiles; two splits (sixteen would read 470 MB of partials back)
-    assert pf(14336, 4096, 512) == partials(14336, 512, 2) + w
-    # 14336x4096 at 1024 and 2048 columns: the tiles cover the chip, no split
+    # 14336x4096 at 512 columns, rebuilt per workgroup in 256-column tiles: 112 tiles, two splits
+    # (sixteen would read 470 MB of partials back)
+    assert pf(14336, 4096, 512) == partials(14336, 512, 2)
+    # 14336x4096 at 1024 and 2048 columns: staged at k = 3, 4; the tiles cover the chip, no split
     assert pf(14336, 4096, 1024) == w
     assert pf(14336, 4096, 2048) == w
-    # below 512 columns nothing is staged; 511 columns of 14336x4096 need no split either
-    assert pf(14336, 4096, 511) == 0
+    # below 1024 columns nothing is staged at k <= 4; 511 columns of 14336x4096 take 256-column tiles
+    # (short inputs), 112 of them, split in two
+    assert pf(14336, 4096, 511) == partials(14336, 511, 2)
+    # 255 columns: 128-column tiles, 112 of them, split in two
+    assert pf(14336, 4096, 255) == partials(14336, 255, 2)
     # a layer of more than 2 GiB of fp16 weight is never staged: partials only, or nothing
     big = pf(65536, 32768, 4096)
     assert big < 65536 * 32768 * 2 and big % 16 == 0
@@ -272,7 +276,7 @@ def test_prefill_rejects_bad_arguments(L):
     assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, None, 0, None) == E_WS
     assert L.aqd_gemm_prefill(FAKE, FAKE, FAKE, 2, FAKE, FAKE, 512, big, FAKE, need - 1, None) == E_WS
     tall = lay(d_out=14336, d_in=4096, M=4)
-    assert L.aqd_gemm_prefill_workspace_bytes(tall, 511) == 0                   # fused, no split
+    assert L.aqd_gemm_prefill_workspace_bytes(lay(d_out=14336, d_in=4096, M=2), 1024) == 0   # fused, no split
     assert L.aqd_gemm_prefill_workspace_bytes(tall, 4096) == 14336 * 4096 * 2   # staged fp16 weights, no split
     assert L.aqd_gemm_prefill_workspace_bytes(big, 0) == 0
 

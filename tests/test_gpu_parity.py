@@ -605,10 +605,12 @@ def test_small_batch_tiered_edge(orc):
     (512, 960, 4, (128,)),            # 15 chunks split one per workgroup: odd chunk counts per split
     (33, 8, 8, (3,)),                 # one group, M = 8, every k
     (600, 8192, 4, (520,)),           # 256-column tiles (batch >= 512, long inputs): ragged rows and columns
-    (40, 600, 3, (600,)),             # fp16 weights staged once (batch >= 512): ragged rows, groups, chunks,
-                                      # columns; one-chunk splits with the zero padding chunk
-    (33, 8, 8, (512,)),               # staged weights: one group (the rest of its tile zeroed), M = 8
-    (1000, 1000, 3, (513,)),          # staged weights: several row blocks, one column past two 256-column tiles
+    (1000, 1000, 3, (300,)),          # 256-column tiles from batch 256 on short inputs
+    (40, 600, 3, (1030,)),            # k = 3: fp16 weights staged once (batch >= 1024): ragged rows, groups,
+                                      # chunks, columns; one-chunk splits with the zero padding chunk
+    (33, 8, 8, (512,)),               # k >= 5 staged from 512 columns: one group (the rest of its tile
+                                      # zeroed), M = 8
+    (1000, 1000, 3, (1100,)),         # k = 3 staged: several row blocks, a ragged last 256-column tile
 ])
 def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(51, extra=d_out * 7 + d_in + M)
@@ -627,14 +629,15 @@ def test_prefill_edge_shapes(orc, d_out, d_in, M, batches):
 
 def test_prefill_dyadic_bit_exact(orc):
     """Exact arithmetic: every split, chunk and column of the tiled product gives the oracle's bits, with
-    the weights rebuilt per workgroup (160 columns) and staged once as fp16 (600 columns)."""
+    the weights rebuilt per workgroup (160 and 600 columns: 128- and 256-column tiles) and, at k = 4,
+    staged once as fp16 (1040 columns)."""
     d_out, d_in, M = 300, 2048, 4
-    codes, cb, s, x = wl.dyadic_case(wl.rng(52), d_out, d_in, M, batch=600)
+    codes, cb, s, x = wl.dyadic_case(wl.rng(52), d_out, d_in, M, batch=1040)
     cdev, cbdev, sdev = _layer_dev(codes, cb, s)
     packed = aqd.aqd_pack_codes(cdev)
     for k in (1, 4):
         ref = orc.linear(codes, cb, s, k, x)
-        for B in (160, 600):
+        for B in (160, 600, 1040):
             y = aqd.aqd_gemm_prefill(packed, cbdev, sdev, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()
             assert np.array_equal(y.astype(np.float64), ref[:B]), (k, B)
 
@@ -647,8 +650,9 @@ def test_prefill_dyadic_bit_exact(orc):
     (4096, 14336, 2048, 2),     # rebuilt per workgroup, 256-column tiles, split inputs
     (4096, 14336, 128, 4),      # rebuilt per workgroup, 128-column tiles, split inputs
     (14336, 4096, 128, 2),
-    (14336, 4096, 512, 4),      # staged weights, two splits
-    (14336, 4096, 2048, 2),     # staged weights, two rounds of workgroups
+    (14336, 4096, 512, 4),      # rebuilt per workgroup, 256-column tiles, two splits
+    (14336, 4096, 2048, 2),     # rebuilt per workgroup, 256-column tiles, two rounds of workgroups
+    (14336, 4096, 2048, 4),     # staged weights, two rounds of workgroups
 ])
 def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
     """Full 8B-shape layers in the launch configuration the benchmark times; eight sampled columns
@@ -673,7 +677,7 @@ def test_prefill_full_size_sampled(orc, d_out, d_in, batch, k):
 def test_prefill_maximum_batch(orc):
     """The largest batch the ABI accepts (AQD_PREFILL_MAX_BATCH columns) on a small layer: columns at the
     ends of 128- and 256-column tiles and the last column against the oracle, and a bit-identical repeat."""
-    B, d_out, d_in, M, k = aqd.AQD_PREFILL_MAX_BATCH, 272, 1024, 2, 2
+    B, d_out, d_in, M, k = aqd.AQD_PREFILL_MAX_BATCH, 272, 1024, 3, 3   # k = 3: staged weights
     g = wl.rng(57)
     codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
     x = wl.gen_x(g, B, d_in, "f16")
