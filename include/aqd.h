@@ -308,10 +308,10 @@ aqd_status aqd_gemm_small_batch(const uint8_t* packed_codes, const uint16_t* cod
  * The weights are fp16 codeword sums (packed fp16 adds in plane order, as the
  * fp16 small-batch mode), multiplied with v_mfma_f32_16x16x32_f16 and
  * accumulated in fp32.  Each workgroup rebuilds its 256 weight rows from the
- * codes up to batch 511, and for d_in >= 8192 also at k <= 2 (any batch) and
- * k = 3, 4 (batch up to 1023).  Otherwise the library first writes the whole
- * fp16 weight (2 * d_out * d_in bytes) into the workspace and the product
- * reads it from there.  Both forms use the same fp16 weights.  Throughput is meant for batch >= 128; any batch
+ * codes at k <= 2 (any batch), at k = 3, 4 up to batch 1023 and at k >= 5 up
+ * to batch 511.  Otherwise the library first writes the whole fp16 weight
+ * (2 * d_out * d_in bytes) into the workspace and the product reads it from
+ * there.  Both forms use the same fp16 weights.  Throughput is meant for batch >= 128; any batch
  * in range is correct.
  *
  * packed_codes, codebooks, scales: as for aqd_gemv; only the first k planes
