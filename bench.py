@@ -425,6 +425,10 @@ def measure_prefill(aqd, wl, torch, dev, reps: int = 5):
             ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
             def timed(fn):
+                # a short idle gap first, so that no case starts on a clock the previous one (the dense
+                # GEMM in particular, at full matrix-core load) has pushed down
+                torch.cuda.synchronize()
+                time.sleep(0.25)
                 for _ in range(2):
                     fn()
                 torch.cuda.synchronize()
