@@ -40,7 +40,7 @@ CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 an
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
 # only for the kernel sources they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30683787
+TRAFFIC_K4_BYTES = 30683297
 TRAFFIC_K4_SOURCE_SHA256_PREFIX = "6828fdc5a6043ece"
 # the batch-1 GEMV kernel's source and the headers it includes
 HEADLINE_SOURCES = ("gemv_lut.hip", "lut_device.h", "fixed_sum.h", "fwht_device.h", "aqd_internal.h")
