@@ -350,11 +350,15 @@ class QuantizedLinear:
         self.packed = aqd_pack_codes(codes)
         self.codebooks = codebooks.contiguous()
         self.scales = scales.contiguous()
-        self.workspace = None
+        # Two buffers, never shared: the GEMV workspace (batch 1..8 and the launch that rotates its own
+        # input) holds counted row sums that must be zero when a call starts and that every call leaves
+        # zero; the small-batch workspace holds split partial sums that every call overwrites.  Handing
+        # the second to a GEMV would leave partial sums where the counters must be zero.
         n = max([aqd_gemv_workspace_bytes(d_out, self.d_in, M, b) for b in range(1, 9)] +
-                [aqd_gemm_small_batch_workspace_bytes(d_out, self.d_in, M, b) for b in range(9, 65)])
-        if n:
-            self.workspace = torch.zeros(n, dtype=torch.uint8, device=codes.device)
+                [aqd_gemv_grouped_workspace_bytes([d_out], self.d_in, [M])])
+        self.workspace = torch.zeros(n, dtype=torch.uint8, device=codes.device) if n else None
+        n = max(aqd_gemm_small_batch_workspace_bytes(d_out, self.d_in, M, b) for b in range(9, 65))
+        self.sb_workspace = torch.empty(n, dtype=torch.uint8, device=codes.device) if n else None
 
     def rotate(self, x2: torch.Tensor) -> torch.Tensor:
         """fp16 rotated activation (with the sign mask when the layer has one)."""
@@ -375,5 +379,6 @@ class QuantizedLinear:
                             workspace=self.workspace)
         if x2.shape[0] <= 64:
             return aqd_gemm_small_batch(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in,
-                                        self.M, AQD_F16, workspace=self.workspace)
+                                        self.M, AQD_F16, workspace=self.sb_workspace)
         return aqd_gemm_prefill(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M)
+

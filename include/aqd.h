@@ -170,7 +170,28 @@ aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, 
  *               start at zero zeroed again, so one buffer of the largest size
  *               needed serves any number of calls, at any batch, on one
  *               stream.  Calls that may overlap in time need separate
- *               workspaces.
+ *               workspaces.  It must not be shared with aqd_gemm_small_batch,
+ *               aqd_gemm_small_batch_tiered or aqd_gemm_prefill, whose
+ *               workspaces hold partial sums.
+ *               A workspace whose first aqd_gemv_workspace_bytes(layer, 1)
+ *               bytes are not zero when a batch-1 or batch-2 call starts (never
+ *               zero-filled, written by another entry point, or left by a call
+ *               whose kernel did not complete) cannot be detected: the rows
+ *               whose words are not zero get undefined outputs (a row may be
+ *               left unwritten or receive a wrong value), the call still
+ *               returns AQD_OK, and those words may stay non-zero for later
+ *               calls.  Zero-filling the workspace again recovers.
+ * Value range of the batch-1 and batch-2 table paths: every table entry
+ * < C_m[c], x_rot[n][8j .. 8j+8) > is rounded to fp16, so its magnitude must
+ * stay below 65504, and entries below 2^-14 (fp16 subnormals) carry an
+ * absolute error of up to 2^-25 each; the partial row sums that travel
+ * between workgroups are fixed point with 24 fraction bits (absolute error
+ * up to 2^-25 per term) and saturate at 2^23.  The error therefore depends on
+ * the product of the activation and codebook scales: for rotated activations
+ * of RMS a and codebook entries of RMS c, the measured normwise error against
+ * an exact product stays below 6e-4 for a * c / 0.05 from 2^-12 up to 2^8
+ * (tested; beyond that the fp16 output of these layers overflows), is about
+ * 1e-3 at 2^-13 and exceeds the 2e-3 bound near 2^-14.
  * Batch 1 and 2 read per-group tables of codeword-activation products (one
  * table per column, built on the matrix cores): one table lookup per code byte
  * and column.  Batch 3..8 with batch * k > 4 runs on the matrix cores (the
