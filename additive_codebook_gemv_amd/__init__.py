@@ -68,6 +68,7 @@ _SIGNATURES = {
     "aqd_gemm_small_batch_workspace_bytes": (_SZ, [_LP, _I32]),
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_tiered": (_INT, [_VP, _VP, _VP, ctypes.POINTER(_I32), _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
+    "aqd_read_probe": (_INT, [_VP, _SZ, _VP, _I32, _I32, _I32, _I32, _VP]),
 }
 
 
@@ -382,3 +383,14 @@ class QuantizedLinear:
                                         self.M, AQD_F16, workspace=self.sb_workspace)
         return aqd_gemm_prefill(self.packed, self.codebooks, self.scales, k, xr, self.d_out, self.d_in, self.M)
 
+
+def aqd_read_probe(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, workgroups: int, waves: int, unroll: int,
+                   contiguous: bool) -> None:
+    """Measurement reference (include/aqd_probe.h): read the first nbytes of buf once with 16-byte loads in
+    one launch of the given shape; sink is int32/uint32 [>= workgroups] and is in practice not written."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink.numel() < workgroups:
+        raise ValueError("sink needs one word per workgroup")
+    _check(lib().aqd_read_probe(_ptr(buf), nbytes, _ptr(sink), workgroups, waves, unroll, int(contiguous),
+                                _stream()))

@@ -1,6 +1,6 @@
 """The C ABI library on the host (no GPU needed).
 
-- libaqd.so loads and exports every function include/aqd.h declares;
+- libaqd.so loads and exports every function the headers under include/ declare;
 - argument validation rejects bad calls with the documented status before
   anything is enqueued (every call here fails validation, so no kernel is
   ever launched on a machine without a GPU);
@@ -17,7 +17,8 @@ import additive_codebook_gemv_amd as aqd
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "aqd.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 OK, E_NULL, E_SHAPE, E_K, E_BLOCK, E_DTYPE, E_ALIGN, E_UNSUP, E_WS, E_HIP = range(10)
 F16, BF16, F32, BF16X2 = 0, 1, 2, 3
@@ -26,9 +27,11 @@ FAKE_ODD = 0x10008  # 8-byte aligned only
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(aqd_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(aqd_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -293,3 +296,17 @@ def test_encode_rejects_bad_arguments(L):
     assert enc(t=FAKE_ODD) == E_ALIGN              # float4 loads
     assert enc(cb=FAKE + 1) == E_ALIGN
     assert enc(d_out=0, t=None) == OK              # nothing to encode
+
+
+def test_read_probe_rejects_bad_arguments(L):
+    probe = L.aqd_read_probe
+    assert probe(FAKE, 0, FAKE, 256, 8, 4, 0, None) == OK                   # nothing to read
+    assert probe(None, 1024, FAKE, 256, 8, 4, 0, None) == E_NULL
+    assert probe(FAKE, 1024, None, 256, 8, 4, 0, None) == E_NULL
+    assert probe(FAKE_ODD, 1024, FAKE, 256, 8, 4, 0, None) == E_ALIGN
+    assert probe(FAKE, 1000, FAKE, 256, 8, 4, 0, None) == E_SHAPE           # not a multiple of 16
+    assert probe(FAKE, 1024, FAKE, 0, 8, 4, 0, None) == E_SHAPE
+    assert probe(FAKE, 1024, FAKE, 65537, 8, 4, 0, None) == E_SHAPE
+    assert probe(FAKE, 1024, FAKE, 256, 17, 4, 0, None) == E_SHAPE
+    assert probe(FAKE, 1024, FAKE, 256, 8, 3, 0, None) == E_SHAPE
+    assert probe(FAKE, 1024, FAKE, 256, 8, 4, 2, None) == E_SHAPE
