@@ -31,40 +31,44 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, int64_t plane
     }
 }
 
+// Grid: x covers the blocks of one row, four per workgroup (one per wave);
+// y strides over the rows.  The block and row indices are wave-uniform.
 template <int B, int IN, int OUT>
 __global__ __launch_bounds__(256) void hadamard_kernel(const void* x, void* y, const uint64_t* signs,
-                                                       int64_t d_in, int64_t n_blocks, int64_t plane) {
+                                                       int32_t blocks_per_row, int64_t batch, int64_t d_in,
+                                                       int64_t plane) {
     constexpr int E = B / 64;
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wave >= n_blocks) return;
-    const int64_t per_row = d_in / B;
-    const int64_t col = (wave % per_row) * B;                  // first input of the block in its row
-    const int64_t base = (wave / per_row) * d_in + col;
-    float v[E];
+    const int blk = (int)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    if (blk >= blocks_per_row) return;
+    const int64_t col = (int64_t)blk * B;                      // first input of the block in its row
+    for (int64_t row = blockIdx.y; row < batch; row += gridDim.y) {
+        const int64_t base = row * d_in + col;
+        float v[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = load_as_f32<IN>(x, base + e * 64 + lane);
-    if (signs) {                                               // uniform: bit `lane` of word (col + 64e) / 64
+        for (int e = 0; e < E; ++e) v[e] = load_as_f32<IN>(x, base + e * 64 + lane);
+        if (signs) {                                           // uniform: bit `lane` of word (col + 64e) / 64
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-            if ((signs[col / 64 + e] >> lane) & 1ull) v[e] = -v[e];
+            for (int e = 0; e < E; ++e)
+                if ((signs[col / 64 + e] >> lane) & 1ull) v[e] = -v[e];
+        }
+        fwht_block<B>(v, lane);
+#pragma unroll
+        for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e]);
     }
-    fwht_block<B>(v, lane);
-#pragma unroll
-    for (int e = 0; e < E; ++e) store_from_f32<OUT>(y, base + e * 64 + lane, plane, v[e]);
 }
 
 template <int B, int IN>
 static hipError_t launch_out(const void* x, void* y, const uint64_t* sg, int out_dt, int64_t batch, int64_t d_in,
                              hipStream_t s) {
-    const int64_t n_blocks = batch * (d_in / B);
+    const int32_t per_row = (int32_t)(d_in / B);
     const int64_t plane = batch * d_in;
-    const dim3 grid((unsigned)((n_blocks + 3) / 4)), block(256);
+    const dim3 grid((unsigned)((per_row + 3) / 4), (unsigned)(batch < 65535 ? batch : 65535)), block(256);
     switch (out_dt) {
-        case AQD_F16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F16>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
-        case AQD_BF16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
-        case AQD_F32: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F32>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
-        default: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16X2>), grid, block, 0, s, x, y, sg, d_in, n_blocks, plane); break;
+        case AQD_F16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F16>), grid, block, 0, s, x, y, sg, per_row, batch, d_in, plane); break;
+        case AQD_BF16: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16>), grid, block, 0, s, x, y, sg, per_row, batch, d_in, plane); break;
+        case AQD_F32: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_F32>), grid, block, 0, s, x, y, sg, per_row, batch, d_in, plane); break;
+        default: hipLaunchKernelGGL((hadamard_kernel<B, IN, AQD_BF16X2>), grid, block, 0, s, x, y, sg, per_row, batch, d_in, plane); break;
     }
     return hipGetLastError();
 }
