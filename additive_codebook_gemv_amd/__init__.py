@@ -69,6 +69,7 @@ _SIGNATURES = {
     "aqd_gemm_small_batch": (_INT, [_VP, _VP, _VP, _I32, _VP, _INT, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_gemm_small_batch_tiered": (_INT, [_VP, _VP, _VP, ctypes.POINTER(_I32), _VP, _VP, _I32, _LP, _VP, _SZ, _VP]),
     "aqd_read_probe": (_INT, [_VP, _SZ, _VP, _I32, _I32, _I32, _I32, _VP]),
+    "aqd_gemv_noalloc": (_INT, [_VP, _VP, _VP, _I32, _VP, _VP, _I32, _LP, _VP]),
 }
 
 
@@ -185,6 +186,23 @@ def aqd_gemv(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor
     _check(lib().aqd_gemv(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x2), _ptr(out), batch,
                           ctypes.byref(L), _ptr(workspace), workspace.numel() if workspace is not None else 0,
                           _stream()))
+    return out
+
+
+AQD_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def aqd_gemv_noalloc(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor, k: int,
+                     x_rot: torch.Tensor, d_out: int, d_in: int, M: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """aqd_gemv with the library's fixed scratch array as workspace (the call itself allocates no device
+    memory; give `out` to allocate nothing here either)."""
+    x2 = x_rot if x_rot.dim() == 2 else x_rot.reshape(1, -1)
+    batch = x2.shape[0]
+    if out is None:
+        out = torch.empty((batch, d_out), dtype=torch.float16, device=x_rot.device)
+    _check(lib().aqd_gemv_noalloc(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x2), _ptr(out), batch,
+                                  ctypes.byref(layer(d_out, d_in, M)), _stream()))
     return out
 
 

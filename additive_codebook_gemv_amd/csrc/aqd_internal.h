@@ -45,6 +45,12 @@ inline Geometry geometry(const aqd_layer& L) {
 
 // Per-thread error text (set by the C entry points).
 void set_error(const std::string& s);
+// aqd_gemv's argument checks without the workspace pointer (ws_bytes available); *need = workspace bytes
+aqd_status check_gemv_args(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int32_t k,
+                           const uint16_t* x_rot, const uint16_t* y, int32_t batch, const aqd_layer* layer,
+                           size_t ws_bytes, size_t* need, bool* nothing);
+// AQD_OK for hipSuccess, else AQD_ERR_HIP with the text in the per-thread error
+aqd_status hip_fail(hipError_t e, const char* what);
 
 // ---- launchers (return hipSuccess or the launch error) --------------------
 hipError_t launch_pack(const uint8_t* codes, uint8_t* packed, const Geometry& g, hipStream_t s);
@@ -54,6 +60,9 @@ hipError_t launch_unpack(const uint8_t* packed, uint8_t* codes, const Geometry& 
 hipError_t launch_hadamard(const void* x, void* y, int in_dt, int out_dt, int64_t batch, int64_t d_in,
                            int block, const uint8_t* signs, hipStream_t s);
 size_t gemv_workspace_bytes(const Geometry& g, int batch);
+// leading bytes of the GEMV workspace that must be zero when a call starts (the table routes'
+// counted row sums; every call leaves them zero again)
+size_t gemv_zeroed_bytes(const Geometry& g);
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
 size_t gemv_lut_workspace_bytes(const Geometry& g);

@@ -167,6 +167,30 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
                       "aqd_gemv");
 }
 
+}  // extern "C"
+
+namespace aqd {
+
+// aqd_gemv's checks for an entry point that supplies a workspace of ws_bytes itself (the no-alloc
+// entry point): everything except the workspace pointer, plus the size limit.
+aqd_status check_gemv_args(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int32_t k,
+                           const uint16_t* x_rot, const uint16_t* y, int32_t batch, const aqd_layer* layer,
+                           size_t ws_bytes, size_t* need, bool* nothing) {
+    if (batch < 1 || batch > 8) return fail(AQD_ERR_SHAPE, "batch must be in [1, 8]");
+    *need = layer ? aqd_gemv_workspace_bytes(layer, batch) : 0;
+    // the workspace pointer is the caller's to check: none is required here
+    aqd_status st = check_product(packed, codebooks, scales, k, x_rot, y, layer, nullptr, 0, 0, nothing);
+    if (st != AQD_OK || *nothing) return st;
+    if (*need > ws_bytes) return fail(AQD_ERR_WORKSPACE, "layer and batch need more workspace than the fixed limit");
+    return AQD_OK;
+}
+
+aqd_status hip_fail(hipError_t e, const char* what) { return hip_status(e, what); }
+
+}  // namespace aqd
+
+extern "C" {
+
 static aqd_status check_group(const aqd_linear* lins, int32_t n, int64_t d_in, aqd_layer* layers) {
     if (!lins) return fail(AQD_ERR_NULL, "linears is NULL");
     if (n < 1 || n > AQD_MAX_GROUP) return fail(AQD_ERR_SHAPE, "n_linears must be in [1, AQD_MAX_GROUP]");

@@ -164,6 +164,8 @@ static size_t lut_region(const Geometry& g) {
     return ((b1 > b2 ? b1 : b2) + 255) & ~(size_t)255;
 }
 
+size_t gemv_zeroed_bytes(const Geometry& g) { return lut_region(g); }
+
 size_t gemv_workspace_bytes(const Geometry& g, int batch) {
     return lut_region(g) + (batch >= 2 ? gemm_sb_workspace_bytes(g, batch) : 0);
 }

@@ -210,6 +210,30 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
                     const aqd_layer* layer, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * aqd_gemv for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument, and the call allocates nothing (no hipMalloc, no
+ * allocating library routine).  Its workspace is a fixed device array inside
+ * the library, AQD_NOALLOC_SCRATCH_BYTES on every GPU it runs on, held until
+ * the process ends; the first call on a device looks up that device's copy.
+ * Every call clears the part that must start at zero with a small fill kernel
+ * on `stream` (one launch more than aqd_gemv), then runs exactly aqd_gemv's
+ * kernels: outputs have aqd_gemv's bits.
+ *
+ * All calls on one GPU share its array: calls that may overlap in time (on
+ * different streams, or from several threads) race and give undefined outputs.
+ * Layers whose aqd_gemv_workspace_bytes(layer, batch) exceeds
+ * AQD_NOALLOC_SCRATCH_BYTES are rejected with AQD_ERR_WORKSPACE before anything
+ * is enqueued (at batch 8 the limit covers about 28 thousand output rows; at
+ * batch 1 about a million).  Other arguments and errors as for aqd_gemv.
+ * ------------------------------------------------------------------------- */
+#define AQD_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+aqd_status aqd_gemv_noalloc(const uint8_t* packed_codes, const uint16_t* codebooks, const uint16_t* scales,
+                            int32_t k, const uint16_t* x_rot, uint16_t* y, int32_t batch,
+                            const aqd_layer* layer, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Grouped batch-1 GEMV: up to AQD_MAX_GROUP linears that read the same rotated
  * input (q, k and v of an attention block; gate and up of an MLP) in one
  * launch.  Each linear computes exactly what aqd_gemv computes for it at

@@ -310,3 +310,19 @@ def test_read_probe_rejects_bad_arguments(L):
     assert probe(FAKE, 1024, FAKE, 256, 17, 4, 0, None) == E_SHAPE
     assert probe(FAKE, 1024, FAKE, 256, 8, 3, 0, None) == E_SHAPE
     assert probe(FAKE, 1024, FAKE, 256, 8, 4, 2, None) == E_SHAPE
+
+
+def test_gemv_noalloc_rejects_before_touching_the_device(L):
+    """Every check of aqd_gemv_noalloc runs before the scratch array is looked up or anything is enqueued,
+    so on a machine without a GPU each of these returns its status."""
+    def call(k=1, batch=1, layer=None, y=FAKE, x=FAKE):
+        return L.aqd_gemv_noalloc(FAKE, FAKE, FAKE, k, x, y, batch, layer or lay(64, 256, 2), None)
+    assert call(batch=0) == E_SHAPE
+    assert call(batch=9) == E_SHAPE
+    assert call(k=3) == E_K
+    assert call(y=None) == E_NULL
+    assert call(x=FAKE_ODD) == E_ALIGN
+    assert call(layer=lay(64, 256, 2, group=16)) == E_UNSUP
+    big = lay(1 << 22, 4096, 4)          # workspace above AQD_NOALLOC_SCRATCH_BYTES at batch 8
+    assert L.aqd_gemv_workspace_bytes(big, 8) > aqd.AQD_NOALLOC_SCRATCH_BYTES
+    assert call(batch=8, layer=big) == E_WS
