@@ -5,17 +5,27 @@
 // codewords its k codes select, so its contribution to an output row is
 //     sum_{m<k} T_{m,j}[code(i,j,m)],   T_{m,j}[c] = < C_m[c], xrot[8j .. 8j+8) >.
 // For batch 1 every row reuses the same 256-entry table per (group, codebook),
-// so the product becomes one 2-byte table lookup and half an fp32 add per code
-// byte instead of a 16-byte codeword gather and four dot2 steps.
+// so the product becomes one 2-byte table lookup per code byte instead of a
+// 16-byte codeword gather and four dot2 steps.
 //
 // Work split.  A "slot" is one (group tile, codebook) pair: 64 groups of one
-// plane.  A workgroup owns a slice of 4 consecutive slots and a block of row
-// tiles.  It builds the 4 x 64 tables of its slice with matrix-core products
-// (v_mfma_f32_32x32x8_f16: 32 codewords x 8 elements times 8 elements x 32
-// groups), stores them as fp16 in LDS, then streams its row tiles: lane l of a
-// wave loads the 16 codes of group l for 16 rows for each slot (one coalesced
-// 1 KiB tile per slot), looks up the four table entries of every row and adds
-// them in fp32.
+// plane.  A workgroup owns a slice of S consecutive slots (S = 1 at k = 1, 2 at
+// k = 2, 4 from k = 3; more if a row would otherwise take more than 255
+// contributions) and a block of row tiles.  It builds the S x 64 tables of its
+// slice with matrix-core products (v_mfma_f32_32x32x8_f16: 32 codewords x 8
+// elements times 8 elements x 32 groups) and stores them as fp16 in LDS, then
+// streams its row tiles: lane l of a wave loads the 16 codes of group l for 16
+// rows for each slot (one coalesced 1 KiB tile per slot) and looks up the
+// table entry of every row and slot.  A slot's tables cost the same to build
+// whatever the number of rows that use them, so at small k a workgroup takes
+// fewer slots and more row tiles.
+//
+// Order of requests.  All waves first request their table operands (a few KB
+// that every workgroup reads); each wave requests its first code tile only
+// once its own operands have arrived, and the other tiles after the tables are
+// built.  Requested earlier, code tiles sit in front of the operands of
+// workgroups that are still waiting for them in the memory queues, and every
+// table build waits with them.
 //
 // LDS layout.  Entry (slot s, codeword c, lane l) is the fp16 at byte
 //     (s/2)*64K + c*256 + l*4 + 2*(s%2),
@@ -23,15 +33,17 @@
 // codes never collide, and the address is built from the code byte with one
 // v_perm_b32 (code -> byte 1, lane offset -> byte 0, slot pair -> byte 2).
 //
-// Reduction.  Each lane holds 16 row partials (its group, all slots).  A
-// transposing butterfly (permlane32 swap, permlane16 swap, row mirror, half
-// row mirror, quad DPP) leaves row (l >> 2) summed over the wave in lane l.
-// Each slice adds its row sums into one 64-bit word per row in the workspace
-// (a contribution count plus a fixed-point sum, device-scope integer atomics);
-// the lane whose atomic add completes the count holds the exact total, scales
-// it by s_i, rounds to fp16, writes y and clears the word.  No barrier or
-// counter is needed, results are bit-reproducible, and the workspace is zero
-// again when the kernel ends.
+// Reduction.  The entries of 4 rows and 2 slots of a lane go, as fp16 halves,
+// into the B operand of one v_mfma_f32_16x16x32_f16 whose A operand is a 0/1
+// routing matrix (lut_route in lut_device.h): the products add them over the
+// slots and over four lanes at a time, in fp32, without vector-ALU adds.  A
+// short transposing butterfly over the remaining 16 lanes (fold_quads) leaves
+// row (l >> 2) summed over the wave in lane l.  Each slice adds its row sums
+// into one 64-bit word per row in the workspace (a contribution count plus a
+// fixed-point sum, device-scope integer atomics); the lane whose atomic add
+// completes the count holds the exact total, scales it by s_i, rounds to fp16,
+// writes y and clears the word.  No barrier or counter is needed, results are
+// bit-reproducible, and the workspace is zero again when the kernel ends.
 #include "fwht_device.h"
 #include "lut_device.h"
 
@@ -65,21 +77,30 @@ struct LutArgs {
 // butterflies and rounding of the standalone rotation (same bits), after the
 // optional sign flips of the randomized variant.
 //
+// S is the number of slots a workgroup holds tables for (1, 2 or 4): 64 KiB of
+// LDS per pair of slots (S = 1 uses half of one pair's entries).  Building a
+// slot's tables costs the same whatever the row count, so a launch with few
+// slots (small k) takes fewer slots and more row tiles per workgroup.
+//
 // The fields the first loads depend on come first, as scalars, so that the
 // launch preloads them into SGPRs (kernel-argument preloading; a by-value
 // struct cannot be preloaded): a workgroup then issues its table operand and
 // code loads without first waiting for an argument load.  packed0, codebooks0,
 // plane_bytes0, n_rt0 and tpb0 are those of linear 0, which a single-linear
-// launch uses; the other fields stay in the struct.
-template <int WAVES, int K, bool MULTI, int HB, int TPW>
+// launch uses; the other fields stay in the struct and are read after the
+// table build.
+template <int WAVES, int K, bool MULTI, int HB, int TPW, int S>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __restrict__ packed0,
                                                               const uint16_t* __restrict__ codebooks0,
                                                               const uint16_t* __restrict__ xin, int64_t plane_bytes0,
                                                               int n_rt0, int G, int slices, int n_slots, int tpb0,
                                                               LutArgs p) {
-    constexpr int XS_BYTES = HB > 0 ? LUT_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
-    __shared__ __align__(16) uint8_t lds[LUT_BYTES + XS_BYTES + 16];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + LUT_BYTES);              // [slot][512]
+    static_assert(S == 1 || S == 2 || S == 4, "slots per workgroup");
+    constexpr int NPAIR = S >= 2 ? S / 2 : 1;                      // 64 KiB table regions
+    constexpr int H = S >= 2 ? 2 : 1;                              // slots per region
+    constexpr int XS_BYTES = HB > 0 ? S * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
+    __shared__ __align__(16) uint8_t lds[NPAIR * LUT_PAIR_BYTES + XS_BYTES + 16];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + NPAIR * LUT_PAIR_BYTES);   // [slot][512]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -91,44 +112,45 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         for (int i = 1; i < LUT_MAX_GROUP; ++i)
             if (i < p.n_lin && (int)blockIdx.x >= p.lin[i].wg_begin) l = i;
     }
-    const LutLinear L = p.lin[MULTI ? l : 0];
-    const uint8_t* const packed = MULTI ? L.packed : packed0;
-    const uint16_t* const codebooks = MULTI ? L.codebooks : codebooks0;
-    const int64_t plane_bytes = MULTI ? L.plane_bytes : plane_bytes0;
-    const int64_t n_rt = MULTI ? L.n_rt : (int64_t)n_rt0;
-    const int tiles_per_block = MULTI ? L.tiles_per_block : tpb0;
-    const int local = (int)blockIdx.x - (MULTI ? L.wg_begin : 0);
+    const uint8_t* const packed = MULTI ? p.lin[l].packed : packed0;
+    const uint16_t* const codebooks = MULTI ? p.lin[l].codebooks : codebooks0;
+    const int64_t plane_bytes = MULTI ? p.lin[l].plane_bytes : plane_bytes0;
+    const int64_t n_rt = MULTI ? p.lin[l].n_rt : (int64_t)n_rt0;
+    const int tiles_per_block = MULTI ? p.lin[l].tiles_per_block : tpb0;
+    const int local = (int)blockIdx.x - (MULTI ? p.lin[l].wg_begin : 0);
     const int slice = local % slices;
     const int rb = local / slices;
     const int64_t t0 = (int64_t)rb * tiles_per_block;
     const int64_t t1 = t0 + tiles_per_block < n_rt ? t0 + tiles_per_block : n_rt;
 
-    // slot s of this slice: q = slice*4 + s -> group tile q / K, codebook q % K.
+    // slot s of this slice: q = slice*S + s -> group tile q / K, codebook q % K.
     // Every load below is unconditional (inactive slots, padding groups and
     // missing tiles read a valid address and the value is replaced by zero), so
     // the compiler can wait for exactly the loads a step needs.
-    __amdgpu_buffer_rsrc_t slot_buf[LUT_SLOTS];
-    bool slot_on[LUT_SLOTS];
+    __amdgpu_buffer_rsrc_t slot_buf[S];
+    bool slot_on[S];
 #pragma unroll
-    for (int s = 0; s < LUT_SLOTS; ++s) {
-        const int q = slice * LUT_SLOTS + s;
+    for (int s = 0; s < S; ++s) {
+        const int q = slice * S + s;
         slot_on[s] = q < n_slots;
         const int qq = slot_on[s] ? q : 0;
         slot_buf[s] = slot_rsrc(packed + (int64_t)(qq % K) * plane_bytes + (int64_t)(qq / K) * n_rt * TILE_BYTES,
                                 n_rt * TILE_BYTES);
     }
 
-    // ---- table operands first (loads complete in order)
-    constexpr int ITEMS = 32 / WAVES;
-    uint2 av[ITEMS][2], bv[ITEMS][2];
-    bool bok[ITEMS][2];
+    // ---- table operands first.  An item is a 32 x 32 block of one region:
+    // codewords 32*cb .. +32 of both slots of pair `pair`, groups 32*gb .. +32.
+    constexpr int ITEMS = 16 * NPAIR / WAVES;
+    static_assert(ITEMS * WAVES == 16 * NPAIR, "items per wave");
+    uint2 av[ITEMS][H], bv[ITEMS][H];
+    bool bok[ITEMS][H];
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
         const int item = wave + u * WAVES;
         const int cb = (item >> 1) & 7, gb = item & 1, pair = item >> 4;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int q = slice * LUT_SLOTS + 2 * pair + h;
+        for (int h = 0; h < H; ++h) {
+            const int q = slice * S + 2 * pair + h;
             const int qq = q < n_slots ? q : 0;
             const int e0 = 4 * (lane >> 5);
             const int c = cb * 32 + (lane & 31);
@@ -136,13 +158,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
             bok[u][h] = q < n_slots && g < G;
             const int64_t gc = g < G ? g : G - 1;
             av[u][h] = *reinterpret_cast<const uint2*>(codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
-            if (HB == 0) bv[u][h] = *reinterpret_cast<const uint2*>(xin + gc * GROUP + e0);
+            // when K is a multiple of S every slot of the slice lies in one group tile, and the
+            // items of a wave share gb: one activation fragment serves them all
+            constexpr bool ONE_TILE = K % S == 0;
+            if (HB == 0) {
+                if (!ONE_TILE || (u == 0 && h == 0)) bv[u][h] = *reinterpret_cast<const uint2*>(xin + gc * GROUP + e0);
+                else bv[u][h] = bv[0][0];
+            }
         }
     }
     // raw activation blocks for the rotation: slot s needs inputs 512*tile .. +512 (tile = q / K),
     // i.e. 512 / HB blocks; wave w takes blocks w, w + WAVES, ...
     constexpr int BLK_PER_SLOT = HB > 0 ? TILE_GROUPS * GROUP / HB : 1;
-    constexpr int NBLK = LUT_SLOTS * BLK_PER_SLOT;
+    constexpr int NBLK = S * BLK_PER_SLOT;
     constexpr int BPW = (NBLK + WAVES - 1) / WAVES;
     constexpr int E = HB > 0 ? HB / 64 : 1;
     float xv[BPW][E];
@@ -152,7 +180,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         for (int b = 0; b < BPW; ++b) {
             const int blk = wave + b * WAVES;
             const int sl = (blk < NBLK ? blk : 0) / BLK_PER_SLOT, j = (blk < NBLK ? blk : 0) % BLK_PER_SLOT;
-            const int q = slice * LUT_SLOTS + sl;
+            const int q = slice * S + sl;
             const int64_t in0 = (int64_t)((q < n_slots ? q : 0) / K) * (TILE_GROUPS * GROUP) + (int64_t)j * HB;
             xok[b] = blk < NBLK && q < n_slots && in0 < (int64_t)G * GROUP;
 #pragma unroll
@@ -165,31 +193,38 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         }
     }
 
-    // Vector memory requests of a CU are served in issue order, so a wave's table
-    // operands would otherwise queue behind the code tiles other waves issued
-    // earlier and the build could only start once the whole stream had arrived.
-    // Every wave issues its operand loads before any wave issues a code load.
+    // The code stream is requested only once this wave's table operands have
+    // arrived.  The operands are a few KB that every workgroup reads; requested
+    // behind the code stream they would wait for a large part of it in the
+    // memory queues, and every table build with them.  All waves of the
+    // workgroup issue their operand loads first (barrier), then each wave waits
+    // for its own.
     __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int u = 0; u < ITEMS; ++u)
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            asm volatile("" ::"v"(av[u][h].x), "v"(av[u][h].y) : "memory");
+            if (HB == 0) asm volatile("" ::"v"(bv[u][h].x), "v"(bv[u][h].y) : "memory");
+        }
+    if (HB > 0) {
+#pragma unroll
+        for (int b = 0; b < BPW; ++b)
+#pragma unroll
+            for (int e = 0; e < E; ++e) asm volatile("" ::"v"(xv[b][e]) : "memory");
+    }
 
-    // ---- then the first code tile of every wave: half of the workgroup's code
-    // stream is in flight while the tables are built.  The second half is
-    // requested only after the build (below): requests issued earlier would sit
-    // in front of other workgroups' table operands and delay every build.
-    uint4 codes[TPW][LUT_SLOTS];
+    // ---- then the first code tile of every wave, in flight while the tables are
+    // built; the other tiles are requested after the build (below), so that
+    // workgroups still waiting for their operands are not queued behind them.
+    uint4 codes[TPW][S];
     auto load_tile = [&](int u) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
         const uint32_t off = it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE;
 #pragma unroll
-        for (int s = 0; s < LUT_SLOTS; ++s) codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
+        for (int s = 0; s < S; ++s) codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
     };
     load_tile(0);
-    // scales of the rows this lane may finish (needed only at the end; clamped)
-    uint16_t row_scale[TPW];
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
-        row_scale[u] = L.scales[row < L.d_out ? row : L.d_out - 1];
-    }
     if (HB > 0) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
@@ -205,7 +240,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
             const int item = wave + u * WAVES;
             const int gb = item & 1, pair = item >> 4;
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < H; ++h)
                 bv[u][h] = *reinterpret_cast<const uint2*>(xs + (2 * pair + h) * (TILE_GROUPS * GROUP) +
                                                            (gb * 32 + (lane & 31)) * GROUP + 4 * (lane >> 5));
         }
@@ -213,17 +248,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < H; ++h) {
             if (!bok[u][h]) bv[u][h] = make_uint2(0u, 0u);     // zero activation -> zero table entries
         }
 
+    // ---- tables: entry (slot s, codeword c, lane l) at byte (s/2)*64K + c*256 + l*4 + 2*(s%2)
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
         const int item = wave + u * WAVES;
         const int pair = item >> 4, cb = (item >> 1) & 7, gb = item & 1;
-        floatx16_t t[2];
+        floatx16_t t[H];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < H; ++h) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) t[h][r] = 0.f;
             t[h] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(half4_t, av[u][h]),
@@ -233,19 +269,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = cb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const half2_t v = half2_t{(_Float16)t[0][r], (_Float16)t[1][r]};
-            *reinterpret_cast<half2_t*>(lds + pair * LUT_PAIR_BYTES + c * 256 + gl * 4) = v;
+            uint8_t* dst = lds + pair * LUT_PAIR_BYTES + c * 256 + gl * 4;
+            if constexpr (H == 2) *reinterpret_cast<half2_t*>(dst) = half2_t{(_Float16)t[0][r], (_Float16)t[H - 1][r]};
+            else *reinterpret_cast<_Float16*>(dst) = (_Float16)t[0][r];
         }
     }
     __syncthreads();
 #pragma unroll
     for (int u = 1; u < TPW; ++u) load_tile(u);
 
-    uint32_t base[LUT_SLOTS];
+    const LutLinear L = p.lin[MULTI ? l : 0];
+    // scales of the rows this lane may finish (needed only at the end; clamped)
+    uint16_t row_scale[TPW];
 #pragma unroll
-    for (int s = 0; s < LUT_SLOTS; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
-    const half2_t ones = half2_t{(_Float16)1.0f, (_Float16)1.0f};
-    const float one = opaque_one();
+    for (int u = 0; u < TPW; ++u) {
+        const int64_t row = (t0 + wave + (int64_t)u * WAVES) * TILE_ROWS + (lane >> 2);
+        row_scale[u] = L.scales[row < L.d_out ? row : L.d_out - 1];
+    }
+
+    uint32_t base[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
+    half8_t route[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) route[q] = lut_route(q, lane);
 
     // returned accumulator words are examined only after the last tile, so the
     // atomics' round trips overlap the remaining lookups
@@ -261,28 +308,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     for (int u = 0; u < TPW; ++u) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
         if (it >= t1) break;                   // uniform across the wave
-        float rows[16];
+        // per row quad q and slot pair: the entries (4 rows x the pair's slots) of this lane in the
+        // fp16 halves of the B operand; one product routes them into D (lut_route)
+        floatx4_t d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float a = 0.f;
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int pr = 0; pr < LUT_SLOTS / 2; ++pr) {
-                const uint4& c0 = codes[u][2 * pr];
-                const uint4& c1 = codes[u][2 * pr + 1];
-                const uint32_t w0 = (r >> 2) == 0 ? c0.x : (r >> 2) == 1 ? c0.y : (r >> 2) == 2 ? c0.z : c0.w;
-                const uint32_t w1 = (r >> 2) == 0 ? c1.x : (r >> 2) == 1 ? c1.y : (r >> 2) == 2 ? c1.z : c1.w;
-                const uint32_t a0 = lut_addr(w0, base[2 * pr], r & 3);
-                const uint32_t a1 = lut_addr(w1, base[2 * pr + 1], r & 3);
-                const _Float16 e0 = *reinterpret_cast<const _Float16*>(lds + a0);
-                const _Float16 e1 = *reinterpret_cast<const _Float16*>(lds + a1);
-                // the first pair as one mixed-precision fma (fp16 inputs, fp32 sum), the others
-                // packed into one v_dot2 each
-                a = pr == 0 ? __builtin_fmaf((float)e0, one, (float)e1)
-                            : __builtin_amdgcn_fdot2(half2_t{e0, e1}, ones, a, false);
+            for (int pr = 0; pr < NPAIR; ++pr) {
+                const uint4& c0 = codes[u][H * pr];
+                const uint4& c1 = codes[u][H * pr + H - 1];
+                const uint32_t w0 = q == 0 ? c0.x : q == 1 ? c0.y : q == 2 ? c0.z : c0.w;
+                const uint32_t w1 = q == 0 ? c1.x : q == 1 ? c1.y : q == 2 ? c1.z : c1.w;
+                half8_t b;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    b[2 * m] = *reinterpret_cast<const _Float16*>(lds + lut_addr(w0, base[H * pr], m));
+                    b[2 * m + 1] = H == 2 ? *reinterpret_cast<const _Float16*>(lds + lut_addr(w1, base[H * pr + H - 1], m))
+                                          : (_Float16)0.0f;
+                }
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[q], b, d, 0, 0, 0);
             }
-            rows[r] = a;
         }
-        const float sum = fold_rows(rows, lane);
+        const float sum = fold_quads(d, lane);
         const int64_t row = it * TILE_ROWS + (lane >> 2);
         if ((lane & 3) == 0 && row < L.d_out) {
             mine[u] = true;
@@ -325,27 +372,46 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
     return b;
 }
 
-template <bool MULTI, int HB, int TPW>
-static void launch_k(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
-    switch (k) {
+// Slots per workgroup: as many as k (1, 2, then 4), more when the slices would
+// exceed what a row's counted sum allows.
+static int lut_slots_for(int64_t n_gt, int k) {
+    int S = k <= 1 ? 1 : (k == 2 ? 2 : 4);
+    while (S < 4 && lut_slices(n_gt, k, S) > LUT_MAX_SLICES) S *= 2;
+    return S;
+}
+
 #define AQD_LUT_ARGS a.lin[0].packed, a.lin[0].codebooks, a.x, a.lin[0].plane_bytes, (int)a.lin[0].n_rt, (int)a.G, \
                      a.slices, a.n_slots, a.lin[0].tiles_per_block, a
-        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB, TPW>), gd, bd, 0, s, AQD_LUT_ARGS); break;
-#undef AQD_LUT_ARGS
+
+template <bool MULTI, int HB, int TPW, int S>
+static void launch_kl(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
+    switch (k) {
+        case 1: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 2: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 3: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 4: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 5: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 5, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 6: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 6, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        case 7: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 7, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
+        default: hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 8, MULTI, HB, TPW, S>), gd, bd, 0, s, AQD_LUT_ARGS); break;
     }
 }
 
+// S = 1 only occurs at k = 1 and S = 2 only at k <= 2 (lut_slots_for), so only
+// those instantiations exist.
+template <bool MULTI, int HB, int TPW>
+static void launch_k(int k, int S, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
+    if (S == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW, 1>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else if (S == 2 && k == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else if (S == 2) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else launch_kl<MULTI, HB, TPW, 4>(k, gd, bd, s, a);
+}
+#undef AQD_LUT_ARGS
+
 template <bool MULTI, int HB>
-static void launch_tpw(int tpw, int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
-    if (tpw == LUT_TILES_PER_WAVE_BIG) launch_k<MULTI, HB, LUT_TILES_PER_WAVE_BIG>(k, gd, bd, s, a);
-    else launch_k<MULTI, HB, LUT_TILES_PER_WAVE>(k, gd, bd, s, a);
+static void launch_tpw(int tpw, int k, int S, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
+    if (tpw == LUT_TILES_PER_WAVE_BIG) launch_k<MULTI, HB, LUT_TILES_PER_WAVE_BIG>(k, S, gd, bd, s, a);
+    else launch_k<MULTI, HB, LUT_TILES_PER_WAVE>(k, S, gd, bd, s, a);
 }
 
 hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
@@ -359,7 +425,8 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
     a.n_gt = n_gt;
     a.k = k;
     a.n_slots = (int)((int64_t)k * n_gt);
-    a.slices = lut_slices(n_gt, k);
+    const int S = lut_slots_for(n_gt, k);
+    a.slices = lut_slices(n_gt, k, S);
     int64_t n_rt[LUT_MAX_GROUP];
     int tpb[LUT_MAX_GROUP], blocks[LUT_MAX_GROUP];
     int m = 0;                                 // linears with rows
@@ -400,12 +467,12 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
     // one linear: the instantiation that takes every field its first loads need from the preloaded
     // leading arguments
     const bool one = m == 1;
-    if (rotate_block == 64) one ? launch_tpw<false, 64>(tpw, k, gd, bd, s, a) : launch_tpw<true, 64>(tpw, k, gd, bd, s, a);
+    if (rotate_block == 64) one ? launch_tpw<false, 64>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 64>(tpw, k, S, gd, bd, s, a);
     else if (rotate_block == 128)
-        one ? launch_tpw<false, 128>(tpw, k, gd, bd, s, a) : launch_tpw<true, 128>(tpw, k, gd, bd, s, a);
+        one ? launch_tpw<false, 128>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 128>(tpw, k, S, gd, bd, s, a);
     else if (rotate_block == 256)
-        one ? launch_tpw<false, 256>(tpw, k, gd, bd, s, a) : launch_tpw<true, 256>(tpw, k, gd, bd, s, a);
-    else one ? launch_tpw<false, 0>(tpw, k, gd, bd, s, a) : launch_tpw<true, 0>(tpw, k, gd, bd, s, a);
+        one ? launch_tpw<false, 256>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 256>(tpw, k, S, gd, bd, s, a);
+    else one ? launch_tpw<false, 0>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 0>(tpw, k, S, gd, bd, s, a);
     return hipGetLastError();
 }
 

@@ -8,6 +8,8 @@
 namespace aqd {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 constexpr int LUT_SLOTS = 4;
@@ -88,6 +90,52 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
     d += dpp<0xB1>(d);                     // quad: lanes 4q..4q+3 hold the same row
     d += dpp<0x4E>(d);
     return d;
+}
+
+// Row sums of a code tile on the matrix cores.
+//
+// Lane l (group l of the tile) holds table entries e[r][s] for the 16 rows r
+// and the slots s of its slice.  v_mfma_f32_16x16x32_f16 takes, per lane, 8
+// fp16 B values B[8*(l>>4) + h][l & 15] and 8 A values A[l & 15][8*(l>>4) + h].
+// With B = (row 4q + m, slot 2p + hs) at h = 2m + hs, and A_q the 0/1 matrix
+// A_q[i][8g + 2m + hs] = [i == 4q + m], one product adds, into D[4q + m][j],
+// the entries of row 4q + m, slots 2p and 2p + 1, of the four lanes j + 16g.
+// Over the row quads q and slot pairs p, D[i][j] = sum over g and s of the
+// entries of row i in lane j + 16g: the sums over slots and over the lane
+// groups cost no vector-ALU instruction, only the 16 lanes j remain.
+//
+// lut_route(): lane l's operand A_q, nonzero only for q = (l & 15) >> 2, in the
+// dword (l & 3): two fp16 ones.
+__device__ __forceinline__ half8_t lut_route(int q, int lane) {
+    const int i = lane & 15;
+    uint32_t d[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) d[m] = i == 4 * q + m ? 0x3C003C00u : 0u;
+    return __builtin_bit_cast(half8_t, make_uint4(d[0], d[1], d[2], d[3]));
+}
+
+// D as left by the products above: lane l holds D[4*(l>>4) + r][l & 15],
+// r = 0..3.  Returns, in lane l, the sum over the 16 lanes of its 16-lane row
+// of D[l >> 2][.] : row (l >> 2) of the tile summed over all 64 groups, the
+// layout fold_rows() leaves.  Each step keeps half of the rows and adds the
+// partner's copy of them (partner j <-> 15 - j, then j <-> 7 - j, then the
+// quad), so rows are transposed into lanes as they are summed.
+__device__ __forceinline__ float fold_quads(const floatx4_t& d, int lane) {
+    const bool lo8 = (lane & 8) == 0;
+    float c[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = lo8 ? d[i] : d[i + 2];
+        const float send = lo8 ? d[i + 2] : d[i];
+        c[i] = keep + dpp<0x140>(send);
+    }
+    const bool lo4 = (lane & 4) == 0;
+    const float keep = lo4 ? c[0] : c[1];
+    const float send = lo4 ? c[1] : c[0];
+    float e = keep + dpp<0x141>(send);
+    e += dpp<0xB1>(e);
+    e += dpp<0x4E>(e);
+    return e;
 }
 
 // 1.0f in a scalar register the compiler cannot see through, so that
