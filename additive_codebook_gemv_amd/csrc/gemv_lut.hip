@@ -33,10 +33,12 @@
 // codes never collide, and the address is built from the code byte with one
 // v_perm_b32 (code -> byte 1, lane offset -> byte 0, slot pair -> byte 2).
 //
-// Reduction.  The entries of 4 rows and 2 slots of a lane go, as fp16 halves,
-// into the B operand of one v_mfma_f32_16x16x32_f16 whose A operand is a 0/1
+// Reduction.  The entries of 4 rows and one slot of a lane, each in the low
+// half of the dword its 2-byte LDS read returns (the high half is zero), are
+// the B operand of one v_mfma_f32_16x16x32_f16 whose A operand is a 0/1
 // routing matrix (lut_route in lut_device.h): the products add them over the
-// slots and over four lanes at a time, in fp32, without vector-ALU adds.  A
+// slots and over four lanes at a time, in fp32, without vector-ALU adds or
+// packing.  A
 // short transposing butterfly over the remaining 16 lanes (fold_quads) leaves
 // row (l >> 2) summed over the wave in lane l.  Each slice adds its row sums
 // into one 64-bit word per row in the workspace (a contribution count plus a
@@ -199,6 +201,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     // memory queues, and every table build with them.  All waves of the
     // workgroup issue their operand loads first (barrier), then each wave waits
     // for its own.
+    // routing matrices of the row sums (lane arithmetic only).  With 4 slots they are formed here,
+    // while the operands are in flight, which measured faster; with fewer slots the compiler's
+    // placement after the table build measured faster.
+    half8_t route[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        route[q] = lut_route(q, lane);
+        if constexpr (S == 4) {
+            const uint4 rq = __builtin_bit_cast(uint4, route[q]);
+            asm volatile("" ::"v"(rq.x), "v"(rq.y), "v"(rq.z), "v"(rq.w));
+        }
+    }
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
@@ -290,10 +304,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     uint32_t base[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) base[s] = (uint32_t)(lane * 4 + 2 * (s & 1)) | ((uint32_t)(s >> 1) << 16);
-    half8_t route[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) route[q] = lut_route(q, lane);
-
     // returned accumulator words are examined only after the last tile, so the
     // atomics' round trips overlap the remaining lookups
     unsigned long long old_word[TPW], term[TPW];
@@ -314,19 +324,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int pr = 0; pr < NPAIR; ++pr) {
-                const uint4& c0 = codes[u][H * pr];
-                const uint4& c1 = codes[u][H * pr + H - 1];
-                const uint32_t w0 = q == 0 ? c0.x : q == 1 ? c0.y : q == 2 ? c0.z : c0.w;
-                const uint32_t w1 = q == 0 ? c1.x : q == 1 ? c1.y : q == 2 ? c1.z : c1.w;
-                half8_t b;
+            for (int sl = 0; sl < S; ++sl) {
+                const uint4& c = codes[u][sl];
+                const uint32_t w = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
+                // the zero-extended 2-byte reads are the B dwords: entry in the low half, zero above
+                uint32_t e[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    b[2 * m] = *reinterpret_cast<const _Float16*>(lds + lut_addr(w0, base[H * pr], m));
-                    b[2 * m + 1] = H == 2 ? *reinterpret_cast<const _Float16*>(lds + lut_addr(w1, base[H * pr + H - 1], m))
-                                          : (_Float16)0.0f;
-                }
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[q], b, d, 0, 0, 0);
+                for (int m = 0; m < 4; ++m) e[m] = *reinterpret_cast<const uint16_t*>(lds + lut_addr(w, base[sl], m));
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[q], __builtin_bit_cast(half8_t, make_uint4(e[0], e[1], e[2], e[3])),
+                                                           d, 0, 0, 0);
             }
         }
         const float sum = fold_quads(d, lane);

@@ -97,12 +97,14 @@ __device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
 // Lane l (group l of the tile) holds table entries e[r][s] for the 16 rows r
 // and the slots s of its slice.  v_mfma_f32_16x16x32_f16 takes, per lane, 8
 // fp16 B values B[8*(l>>4) + h][l & 15] and 8 A values A[l & 15][8*(l>>4) + h].
-// With B = (row 4q + m, slot 2p + hs) at h = 2m + hs, and A_q the 0/1 matrix
-// A_q[i][8g + 2m + hs] = [i == 4q + m], one product adds, into D[4q + m][j],
-// the entries of row 4q + m, slots 2p and 2p + 1, of the four lanes j + 16g.
-// Over the row quads q and slot pairs p, D[i][j] = sum over g and s of the
-// entries of row i in lane j + 16g: the sums over slots and over the lane
-// groups cost no vector-ALU instruction, only the 16 lanes j remain.
+// With B = (row 4q + m, slot s) at h = 2m and zero at h = 2m + 1 (the dword a
+// 2-byte LDS read returns), and A_q the 0/1 matrix A_q[i][8g + 2m + hs] =
+// [i == 4q + m], one product adds, into D[4q + m][j], the entries of row
+// 4q + m, slot s, of the four lanes j + 16g.  Over the row quads q and the
+// slots s, D[i][j] = sum over g and s of the entries of row i in lane j + 16g:
+// the sums over slots and over the lane groups cost no vector-ALU instruction,
+// only the 16 lanes j remain.  (A second slot in the odd halves would halve the
+// products but cost a pack per pair of entries; measured slower.)
 //
 // lut_route(): lane l's operand A_q, nonzero only for q = (l & 15) >> 2, in the
 // dword (l & 3): two fp16 ones.
