@@ -17,14 +17,17 @@
 // matrix-core product (32 codewords x 8 elements times 8 elements x 32
 // groups), one product per column.
 //
-// Per code byte a lane spends one address and one LDS read, and per pair of
-// slots one mixed-precision fma per column (v_fma_mix_f32 adds the two fp16
-// entries of a column in fp32, picking the dword half by op_sel): 2 VALU
-// operations per code byte, as at batch 1, for twice the output.  Row sums of
-// both columns leave through the counted fixed-point words of batch 1 (one
-// word per column and row): lanes 4q and 4q+1 hold row q's sums after the
-// butterfly and add column 0 and column 1 respectively, so one atomic
-// instruction serves both columns.
+// Per code byte a lane spends one address and one LDS read.  The four dwords
+// read for rows 4q .. 4q+3 of one slot (both columns each) are the B operand
+// of one v_mfma_f32_16x16x32_f16 whose 0/1 A operand routes half h of quad q
+// to output row 8(q mod 2) + h (lut_route2): two accumulators, for quads 0-1
+// and 2-3, collect the sums over slots and over four lanes at a time in fp32,
+// and the batch-1 butterfly over the remaining 16 lanes (fold_quads) leaves
+// output row (l >> 2) of each accumulator in lane l.  Row sums of both columns
+// leave through the counted fixed-point words of batch 1 (one word per column
+// and row): lane 4i adds output row i of the first accumulator and lane 4i+1
+// that of the second, so one atomic instruction serves all 32 (row, column)
+// sums of a tile.
 #include "lut_device.h"
 
 namespace aqd {
@@ -99,10 +102,14 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
     };
     load_tile(0);
     uint16_t row_scale[TPW];
+    {
+        const int oi_ = (lane >> 2) & 15;
+        const int trow_ = ((lane & 3) == 1 ? 8 : 0) + 4 * (oi_ >> 3) + ((oi_ >> 1) & 3);
 #pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + (lane >> 2);
-        row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
+        for (int u = 0; u < TPW; ++u) {
+            const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow_;
+            row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
+        }
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
@@ -137,8 +144,15 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
     uint32_t base[LUT2_SLOTS];
 #pragma unroll
     for (int s = 0; s < LUT2_SLOTS; ++s) base[s] = (uint32_t)(lane * 4) | ((uint32_t)s << 16);
-    const float one = opaque_one();
-    const int col = lane & 1;                   // the column this lane adds after the butterfly
+    half8_t route[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) route[h] = lut_route2(h, lane);
+    // after the butterflies lane l holds output row i = (l >> 2) & 15 of both accumulators; lane 4i
+    // adds the first one's (quads 0-1), lane 4i + 1 the second one's (quads 2-3)
+    const int oi = (lane >> 2) & 15;
+    const int part = lane & 3;
+    const int col = oi & 1;                                                // column of output row i
+    const int trow = (part == 1 ? 8 : 0) + 4 * (oi >> 3) + ((oi >> 1) & 3); // tile row of this lane's sum
 
     unsigned long long old_word[TPW], term[TPW];
     bool mine[TPW];
@@ -152,31 +166,33 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
     for (int u = 0; u < TPW; ++u) {
         const int64_t it = t0 + wave + (int64_t)u * LUT_WAVES;
         if (it >= t1) break;                    // uniform across the wave
-        float r0[16], r1[16];
+        floatx4_t d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const uint4& c0 = codes[u][0];
-            const uint4& c1 = codes[u][1];
-            const uint32_t w0 = (r >> 2) == 0 ? c0.x : (r >> 2) == 1 ? c0.y : (r >> 2) == 2 ? c0.z : c0.w;
-            const uint32_t w1 = (r >> 2) == 0 ? c1.x : (r >> 2) == 1 ? c1.y : (r >> 2) == 2 ? c1.z : c1.w;
-            const half2_t v0 = *reinterpret_cast<const half2_t*>(lds + lut_addr(w0, base[0], r & 3));
-            const half2_t v1 = *reinterpret_cast<const half2_t*>(lds + lut_addr(w1, base[1], r & 3));
-            r0[r] = __builtin_fmaf((float)v0.x, one, (float)v1.x);      // v_fma_mix_f32, fp16 halves in
-            r1[r] = __builtin_fmaf((float)v0.y, one, (float)v1.y);
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int s = 0; s < LUT2_SLOTS; ++s) {
+                const uint4& c = codes[u][s];
+                const uint32_t w = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
+                uint32_t e[4];                  // (column 0, column 1) entries of rows 4q .. 4q+3
+#pragma unroll
+                for (int m = 0; m < 4; ++m) e[m] = *reinterpret_cast<const uint32_t*>(lds + lut_addr(w, base[s], m));
+                d[q >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    route[q & 1], __builtin_bit_cast(half8_t, make_uint4(e[0], e[1], e[2], e[3])), d[q >> 1], 0, 0, 0);
+            }
         }
-        const float s0 = fold_rows(r0, lane);
-        const float s1 = fold_rows(r1, lane);
-        const int64_t row = it * TILE_ROWS + (lane >> 2);
-        if ((lane & 2) == 0 && row < p.d_out) {
+        const float s0 = fold_quads(d[0], lane);
+        const float s1 = fold_quads(d[1], lane);
+        const int64_t row = it * TILE_ROWS + trow;
+        if (part < 2 && row < p.d_out) {
             mine[u] = true;
-            term[u] = fix_term(col ? s1 : s0);
+            term[u] = fix_term(part == 0 ? s0 : s1);
             old_word[u] = atomicAdd(p.acc + col * p.d_out + row, fix_add_word(term[u]));
         }
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         if (!mine[u] || !fix_is_last(old_word[u], p.slices)) continue;
-        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + (lane >> 2);
+        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow;
         p.y[col * p.d_out + row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], p.slices));
         __hip_atomic_store(p.acc + col * p.d_out + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -1,7 +1,8 @@
 // Device helpers shared by the lookup-table GEMV kernels (batch 1 and the
 // two-column variant): the LDS table geometry, streaming loads of code tiles
-// through buffer descriptors, the table address of a code byte, and the
-// transposing butterfly that sums 16 row partials over a wave.
+// through buffer descriptors, the table address of a code byte, the 0/1
+// routing operands that sum table entries on the matrix cores, and the
+// transposing butterfly over the remaining 16 lanes.
 #pragma once
 #include "fixed_sum.h"
 
@@ -50,48 +51,6 @@ __device__ __forceinline__ float dpp(float v) {
     return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float2 swap32(float a, float b) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float2 swap16(float a, float b) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// v[r] = partial of row r in this lane.  Returns, in lane l, the sum over the
-// 64 lanes of row (l >> 2).
-__device__ __forceinline__ float fold_rows(const float (&v)[16], int lane) {
-    float a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {          // lanes 0-31 keep row i, lanes 32-63 keep row i+8
-        const float2 s = swap32(v[i], v[i + 8]);
-        a[i] = s.x + s.y;
-    }
-    float b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {          // even 16-lane rows keep i, odd rows keep i+4
-        const float2 s = swap16(a[i], a[i + 4]);
-        b[i] = s.x + s.y;
-    }
-    const bool lo8 = (lane & 8) == 0;      // partner lane j <-> 15-j inside 16 lanes
-    float c[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const float keep = lo8 ? b[i] : b[i + 2];
-        const float send = lo8 ? b[i + 2] : b[i];
-        c[i] = keep + dpp<0x140>(send);
-    }
-    const bool lo4 = (lane & 4) == 0;      // partner lane j <-> 7-j inside 8 lanes
-    const float keep = lo4 ? c[0] : c[1];
-    const float send = lo4 ? c[1] : c[0];
-    float d = keep + dpp<0x141>(send);
-    d += dpp<0xB1>(d);                     // quad: lanes 4q..4q+3 hold the same row
-    d += dpp<0x4E>(d);
-    return d;
-}
-
 // Row sums of a code tile on the matrix cores.
 //
 // Lane l (group l of the tile) holds table entries e[r][s] for the 16 rows r
@@ -116,11 +75,25 @@ __device__ __forceinline__ half8_t lut_route(int q, int lane) {
     return __builtin_bit_cast(half8_t, make_uint4(d[0], d[1], d[2], d[3]));
 }
 
+// Two activation columns: B dword m holds the (column 0, column 1) entries of
+// row 4q + m, so half h = 2m + c is (row 4q + m, column c).  lut_route2(p)
+// is the A operand with A[i][8g + h] = [i == 8p + h]: with p = q mod 2, one
+// product adds half h of quad q into D[8(q mod 2) + h][j], so two accumulators
+// (quads 0-1 and 2-3) hold the 32 (row, column) sums.
+__device__ __forceinline__ half8_t lut_route2(int p, int lane) {
+    const int i = lane & 15;
+    const uint32_t one = 0x3C00u << (16 * (i & 1));          // the fp16 one, in half (i & 1)
+    uint32_t d[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) d[m] = (i >> 1) == 4 * p + m ? one : 0u;
+    return __builtin_bit_cast(half8_t, make_uint4(d[0], d[1], d[2], d[3]));
+}
+
 // D as left by the products above: lane l holds D[4*(l>>4) + r][l & 15],
 // r = 0..3.  Returns, in lane l, the sum over the 16 lanes of its 16-lane row
-// of D[l >> 2][.] : row (l >> 2) of the tile summed over all 64 groups, the
-// layout fold_rows() leaves.  Each step keeps half of the rows and adds the
-// partner's copy of them (partner j <-> 15 - j, then j <-> 7 - j, then the
+// of D[l >> 2][.] : output row (l >> 2) summed over all 64 groups, the same
+// value in the four lanes of a quad.  Each step keeps half of the rows and adds
+// the partner's copy of them (partner j <-> 15 - j, then j <-> 7 - j, then the
 // quad), so rows are transposed into lanes as they are summed.
 __device__ __forceinline__ float fold_quads(const floatx4_t& d, int lane) {
     const bool lo8 = (lane & 8) == 0;
@@ -138,15 +111,6 @@ __device__ __forceinline__ float fold_quads(const floatx4_t& d, int lane) {
     e += dpp<0xB1>(e);
     e += dpp<0x4E>(e);
     return e;
-}
-
-// 1.0f in a scalar register the compiler cannot see through, so that
-// fma((float)h0, one, (float)h1) of two fp16 values stays one v_fma_mix_f32
-// instead of two conversions and an add.
-__device__ __forceinline__ float opaque_one() {
-    float v;
-    asm volatile("s_mov_b32 %0, 1.0" : "=s"(v));
-    return v;
 }
 
 // Row tiles per workgroup for each linear: the grid aims at one workgroup per

@@ -40,9 +40,10 @@ CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 an
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
 # only for the kernel sources they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30680327
-TRAFFIC_K4_SOURCE_SHA256_PREFIX = "ab30a93b0a117e5e"
+TRAFFIC_K4_BYTES = 30676166
+TRAFFIC_K4_SOURCE_SHA256_PREFIX = "09361f69ea2e5d23"
 # the batch-1 GEMV kernel's source and the headers it includes
+TIMING_ROUNDS = 4          # rounds the timed steps are split into (see main)
 HEADLINE_SOURCES = ("gemv_lut.hip", "lut_device.h", "fixed_sum.h", "fwht_device.h", "aqd_internal.h")
 
 
@@ -609,38 +610,53 @@ def main():
             gemv(k)
     torch.cuda.synchronize()
 
-    # The K timed steps are issued kernel-major: K rotations, then K GEMVs at k = 1, then K at k = 2, ...
-    # Every step's work is done exactly once.  Each run of K launches of one kernel is captured in a
-    # graph (a Python launch costs more than a short kernel takes) and the graphs are replayed between
-    # events on the launch stream, so every event pair brackets K launches of one kernel.
-    def capture(fn):
+    # The K timed steps are issued in TIMING_ROUNDS rounds.  Each round replays, in turn, a graph of
+    # about K / TIMING_ROUNDS rotations and one of about K / TIMING_ROUNDS GEMVs at each k (a Python
+    # launch costs more than a short kernel takes), with an event after every graph.  Every step's
+    # work is done exactly once, each kernel's time is the sum of its graphs' event intervals, and no
+    # kernel is always the one timed last (after milliseconds of back-to-back streaming the part can
+    # sustain less than at the start).
+    rounds = max(1, min(TIMING_ROUNDS, args.steps))
+    seg = [args.steps // rounds + (1 if r < args.steps % rounds else 0) for r in range(rounds)]
+
+    def capture(fn, n):
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             with torch.cuda.graph(g, stream=side):
-                for _ in range(args.steps):
+                for _ in range(n):
                     fn()
         stream.wait_stream(side)
         return g
 
-    graphs = [capture(rotate)] + [capture(lambda k=k: gemv(k)) for k in KS]
-    for g in graphs:
-        g.replay()
+    kernels = [rotate] + [lambda k=k: gemv(k) for k in KS]
+    graphs = [[capture(fn, seg[r]) for fn in kernels] for r in range(rounds)]
+    for row in graphs:
+        for g in row:
+            g.replay()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(graphs) + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(rounds * len(kernels) + 1)]
     t0 = time.perf_counter()
     evs[0].record(stream)
-    for i, g in enumerate(graphs):
-        g.replay()
-        evs[i + 1].record(stream)
+    i = 0
+    for row in graphs:
+        for g in row:
+            g.replay()
+            i += 1
+            evs[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = evs[0].elapsed_time(evs[-1])
-    rot_us = evs[0].elapsed_time(evs[1]) * 1e3 / args.steps
+    kernel_ms = [0.0] * len(kernels)
+    for r in range(rounds):
+        for j in range(len(kernels)):
+            e = r * len(kernels) + j
+            kernel_ms[j] += evs[e].elapsed_time(evs[e + 1])
+    rot_us = kernel_ms[0] * 1e3 / args.steps
     per_k = {}
     for i, k in enumerate(KS):
-        us = evs[i + 1].elapsed_time(evs[i + 2]) * 1e3 / args.steps
+        us = kernel_ms[i + 1] * 1e3 / args.steps
         per_k[k] = {
             "us_per_gemv": us,
             "code_bytes": code_bytes(k),
