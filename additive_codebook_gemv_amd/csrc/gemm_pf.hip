@@ -32,14 +32,8 @@ namespace aqd {
 typedef _Float16 pf_half8_t __attribute__((ext_vector_type(8)));
 typedef float pf_floatx4_t __attribute__((ext_vector_type(4)));
 
-#ifndef PF_WAVES_CFG
-#define PF_WAVES_CFG 8
-#endif
-#ifndef PF_PER_CU_CFG
-#define PF_PER_CU_CFG 1
-#endif
-constexpr int PF_WAVES = PF_WAVES_CFG;                   // waves per workgroup
-constexpr int PF_PER_CU = PF_PER_CU_CFG;                 // workgroups resident per compute unit
+constexpr int PF_WAVES = 8;                              // waves per workgroup (4: slower; 16: equal, twice the activation reads)
+constexpr int PF_PER_CU = 1;                              // workgroups resident per compute unit (two spill)
 constexpr int PF_FRAGS = 16 / PF_WAVES;                  // 16-row A fragments per wave
 constexpr int PF_TILES = PF_WAVES * PF_FRAGS;            // 16-row code tiles per workgroup (256 rows)
 constexpr int PF_CHUNK = 64;                             // inputs per staged chunk (8 groups)
