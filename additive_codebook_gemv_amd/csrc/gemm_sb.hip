@@ -280,6 +280,13 @@ __global__ __launch_bounds__(SB_REDUCE_THREADS) void sb_reduce_kernel(const floa
     const int64_t q4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const int64_t nq = (d_out + 3) / 4;
     if (q4 >= nq) return;
+    // the four rows' scales are requested with the partials (clamped rows), not after the sum
+    float sc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t i = 4 * q4 + c;
+        sc[c] = h2f(scales[i < d_out ? i : d_out - 1]);
+    }
     const float4* pq = reinterpret_cast<const float4*>(part) + (int64_t)blockIdx.y * nq + q4;
     const int64_t stride = (int64_t)batch * nq;                 // one split to the next
     float4 v[SB_MAX_SPLITS];
@@ -294,14 +301,23 @@ __global__ __launch_bounds__(SB_REDUCE_THREADS) void sb_reduce_kernel(const floa
             a.z += v[sp].z;
             a.w += v[sp].w;
         }
-    const float sum[4] = {a.x, a.y, a.z, a.w};
+    const float r[4] = {sc[0] * a.x, sc[1] * a.y, sc[2] * a.z, sc[3] * a.w};
+    const int64_t e0 = (int64_t)blockIdx.y * d_out + 4 * q4;
+    if ((d_out & 3) == 0) {                                      // four whole, aligned rows: one store
+        if (out_f16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + e0) =
+                make_uint2((uint32_t)f2h(r[0]) | ((uint32_t)f2h(r[1]) << 16),
+                           (uint32_t)f2h(r[2]) | ((uint32_t)f2h(r[3]) << 16));
+        else
+            *reinterpret_cast<float4*>(static_cast<float*>(y) + e0) = make_float4(r[0], r[1], r[2], r[3]);
+        return;
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-        const int64_t i = 4 * q4 + c;
-        if (i >= d_out) break;
-        const int64_t e = (int64_t)blockIdx.y * d_out + i;
-        if (out_f16) static_cast<uint16_t*>(y)[e] = f2h(h2f(scales[i]) * sum[c]);
-        else static_cast<float*>(y)[e] = h2f(scales[i]) * sum[c];
+        if (4 * q4 + c < d_out) {
+            if (out_f16) static_cast<uint16_t*>(y)[e0 + c] = f2h(r[c]);
+            else static_cast<float*>(y)[e0 + c] = r[c];
+        }
     }
 }
 
