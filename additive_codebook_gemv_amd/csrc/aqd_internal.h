@@ -72,6 +72,10 @@ hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, con
 // batch 2 through the lookup tables: x [2][d_in], y [2][d_out], ws holds [2][d_out] words kept zero
 size_t gemv_lut2_workspace_bytes(const Geometry& g);
 bool gemv_lut2_supported(const Geometry& g, int batch, int k);
+size_t gemv_lut4_workspace_bytes(const Geometry& g);
+bool gemv_lut4_supported(const Geometry& g, int batch, int k);
+hipError_t launch_gemv_lut4(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
+                            const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s);
 hipError_t launch_gemv_lut2(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,
                             const uint16_t* x, uint16_t* y, const Geometry& g, void* ws, hipStream_t s);
 // several batch-1 linears sharing one input and k, in one launch

@@ -1,6 +1,7 @@
 // Decode GEMV, batch 1..8: lookup-and-accumulate over the packed code tiles
-// (batch 1 through the table kernel, batch 2..8 with batch * k > 4 through the
-// fp16 matrix-core kernel, the rest here).
+// (batch 1 and 2 through the table kernels, batch 3 and 4 at k <= 2 on small
+// slot counts through the four-column tables, otherwise batch 2..8 with
+// batch * k > 4 through the fp16 matrix-core kernel, the rest here).
 //
 // Drop-by-Drop ("Multi-Bitwidth Quantization for LLMs Using Additive
 // Codebooks"), section 3.2: every 8-wide group of a weight row is the sum of
@@ -156,12 +157,15 @@ __global__ __launch_bounds__(64 * GEMV_WAVES) void gemv_direct_kernel(
 // per code of the direct kernel.
 static bool gemv_use_mfma(int batch, int k) { return batch >= 2 && batch * k > 4; }
 
-// The lookup-table accumulators of batch 1 and 2 (which must stay zero between
+// The lookup-table accumulators of batch 1..4 (which must stay zero between
 // calls) come first; the matrix-core route's partial sums (overwritten by every
 // call) follow.
 static size_t lut_region(const Geometry& g) {
-    const size_t b1 = gemv_lut_workspace_bytes(g), b2 = gemv_lut2_workspace_bytes(g);
-    return ((b1 > b2 ? b1 : b2) + 255) & ~(size_t)255;
+    size_t b = gemv_lut_workspace_bytes(g);
+    const size_t b2 = gemv_lut2_workspace_bytes(g), b4 = gemv_lut4_workspace_bytes(g);
+    b = b2 > b ? b2 : b;
+    b = b4 > b ? b4 : b;
+    return (b + 255) & ~(size_t)255;
 }
 
 size_t gemv_zeroed_bytes(const Geometry& g) { return lut_region(g); }
@@ -184,6 +188,7 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* codebooks, const u
                        const uint16_t* x, uint16_t* y, int batch, const Geometry& g, void* ws, hipStream_t s) {
     if (gemv_lut_supported(g, batch, k)) return launch_gemv_lut(packed, codebooks, scales, k, x, y, g, ws, s);
     if (gemv_lut2_supported(g, batch, k)) return launch_gemv_lut2(packed, codebooks, scales, k, x, y, g, ws, s);
+    if (gemv_lut4_supported(g, batch, k)) return launch_gemv_lut4(packed, codebooks, scales, k, x, y, batch, g, ws, s);
     if (gemv_use_mfma(batch, k))
         return launch_gemm_sb_f16out(packed, codebooks, scales, k, x, y, batch, g,
                                      ws ? static_cast<uint8_t*>(ws) + lut_region(g) : nullptr, s);

@@ -174,14 +174,16 @@ aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, 
  *               aqd_gemm_small_batch_tiered or aqd_gemm_prefill, whose
  *               workspaces hold partial sums.
  *               A workspace whose first aqd_gemv_workspace_bytes(layer, 1)
- *               bytes are not zero when a batch-1 or batch-2 call starts (never
+ *               bytes are not zero when a call on a table route starts (batch
+ *               1 and 2; batch 3 and 4 at k <= 2 on layers of at most 32 table
+ *               slots, i.e. k * ceil(d_in / 512) <= 32) (never
  *               zero-filled, written by another entry point, or left by a call
  *               whose kernel did not complete) cannot be detected: the rows
  *               whose words are not zero get undefined outputs (a row may be
  *               left unwritten or receive a wrong value), the call still
  *               returns AQD_OK, and those words may stay non-zero for later
  *               calls.  Zero-filling the workspace again recovers.
- * Value range of the batch-1 and batch-2 table paths: every table entry
+ * Value range of the table routes (batch 1..4, above): every table entry
  * < C_m[c], x_rot[n][8j .. 8j+8) > is rounded to fp16, so its magnitude must
  * stay below 65504, and entries below 2^-14 (fp16 subnormals) carry an
  * absolute error of up to 2^-25 each; the partial row sums that travel
@@ -194,11 +196,13 @@ aqd_status aqd_hadamard_rotate_signed(const void* x, void* x_rot, int in_dtype, 
  * 1e-3 at 2^-13 and exceeds the 2e-3 bound near 2^-14.
  * Batch 1 and 2 read per-group tables of codeword-activation products (one
  * table per column, built on the matrix cores): one table lookup per code byte
- * and column.  Batch 3..8 with batch * k > 4 runs on the matrix cores (the
- * fp16 operand mode of aqd_gemm_small_batch, result rounded to fp16); the other
- * cases use codeword lookups with v_dot2 accumulation.  (Inputs too long for the
- * tables, k * ceil(d_in / 512) above 1020 at batch 1 or 510 at batch 2, take
- * the latter routes too.)
+ * (all columns' entries in one read).  Batch 3 and 4 do the same with four
+ * columns per entry where k <= 2 and k * ceil(d_in / 512) <= 32.  Other calls
+ * at batch 2..8 with batch * k > 4 run on the matrix cores (the fp16 operand
+ * mode of aqd_gemm_small_batch, result rounded to fp16); the remaining cases use
+ * codeword lookups with v_dot2 accumulation.  (Inputs too long for the tables,
+ * k * ceil(d_in / 512) above 1020 at batch 1 or 510 at batch 2, take the latter
+ * routes too.)
  * Accumulation is fp32; the summation order is not specified, but it is fixed:
  * repeating a call on the same inputs gives the same bits.
  * packed_codes, x_rot and workspace 16-byte aligned; codebooks 16-byte aligned.
@@ -224,8 +228,9 @@ aqd_status aqd_gemv(const uint8_t* packed_codes, const uint16_t* codebooks, cons
  * different streams, or from several threads) race and give undefined outputs.
  * Layers whose aqd_gemv_workspace_bytes(layer, batch) exceeds
  * AQD_NOALLOC_SCRATCH_BYTES are rejected with AQD_ERR_WORKSPACE before anything
- * is enqueued (at batch 8 the limit covers about 28 thousand output rows; at
- * batch 1 about a million).  Other arguments and errors as for aqd_gemv.
+ * is enqueued (the limit covers about 65 thousand output rows at batch 8 with
+ * 14336 inputs, and about half a million at batch 1).  Other arguments and
+ * errors as for aqd_gemv.
  * ------------------------------------------------------------------------- */
 #define AQD_NOALLOC_SCRATCH_BYTES (16u << 20)
 

@@ -196,8 +196,10 @@ def test_gemv_stack_sampled(orc):
     (1, 8, 1, (1, 2)),                # one row, one group
     (33, 4096, 8, (1, 2, 5)),         # M = 8 codebooks, every k
     (2048, 512, 2, (7,)),
-    (16, 65536, 4, (1, 2)),           # at k = 4 too long for the batch-2 tables (k * d_in / 512 > 510)
-    (16, 130560, 4, (1, 2)),          # 255 table slices, the most a row sum counts: batch 1 at k = 4, batch 2 at k = 2
+    (16, 65536, 4, (1, 2, 4)),        # at k = 4 too long for the batch-2 tables (k * d_in / 512 > 510); batch 4:
+                                      # four-column tables at k = 1 (128 slices), other routes above
+    (16, 130560, 4, (1, 2, 3)),       # 255 table slices, the most a row sum counts: batch 1 at k = 4, batch 2 at k = 2,
+                                      # batch 3 at k = 1
 ])
 def test_gemv_edge_shapes(orc, d_out, d_in, M, batches):
     g = wl.rng(21, extra=d_out * 7 + d_in + M)
@@ -231,7 +233,7 @@ def test_gemv_dyadic_bit_exact(orc, d_out, d_in, M):
     for k in range(1, M + 1):
         ref = orc.linear(codes, cb, s, k, x)
         assert np.max(np.abs(ref)) < 512          # every value and partial sum is exact in fp16/fp32
-        for B in (1, 2, 8):
+        for B in (1, 2, 3, 4, 8):
             y = aqd.aqd_gemv(packed, cbdev, sdev, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()
             assert np.array_equal(y.astype(np.float64), ref[:B]), (k, B)
 

@@ -2,8 +2,9 @@
 
 It must give aqd_gemv's bits on the same inputs, call after call on the shared
 scratch array, the second call with a smaller input, on every route (batch 1
-and 2 through the lookup tables, batch 3..8 on the matrix cores, the
-codeword-gather kernel for inputs too long for the tables), and stay within the
+and 2 through the lookup tables, batch 4 at k = 2 through the four-column
+tables, batch 8 on the matrix cores, the codeword-gather kernel for inputs too
+long for the tables), and stay within the
 oracle's tolerance (Drop-by-Drop, sections 3.2 and 5).  Runs alone in a fresh
 process or after the other tests.
 """
@@ -36,7 +37,7 @@ def _layer(seed, d_out, d_in, M):
 @pytest.mark.parametrize("first,second", [
     ((4096, 14336, 4, 4, 1), (1024, 4096, 4, 2, 1)),    # batch 1 (tables), then a smaller layer
     ((4096, 4096, 4, 3, 2), (300, 1000, 3, 3, 2)),      # batch 2 (two-column tables), ragged second
-    ((14336, 4096, 4, 4, 8), (4096, 4096, 4, 2, 4)),    # batch 8 and 4 on the matrix cores
+    ((14336, 4096, 4, 4, 8), (4096, 4096, 4, 2, 4)),    # batch 8 on the matrix cores, then batch 4 (4-column tables)
     ((16, 65536, 8, 8, 1), (16, 8192, 8, 8, 1)),        # codeword gathers (too long for the tables), then tables
 ])
 def test_noalloc_matches_gemv_twice(orc, first, second):
