@@ -378,10 +378,20 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
     return b;
 }
 
-// Slots per workgroup: as many as k (1, 2, then 4), more when the slices would
-// exceed what a row's counted sum allows.
-static int lut_slots_for(int64_t n_gt, int k) {
+// Slots per workgroup for one linear: as many as k (1, 2, then 4), more when
+// the slices would exceed what a row's counted sum allows.  With 4 slots, a
+// linear too small to give every wave of a workgroup a row tile (fewer tiles
+// per workgroup than waves) takes 2: the 4-slot table build would otherwise
+// sit on the critical path of half-idle workgroups (measured on 4096x4096 at
+// k = 3 and 4: 5.9 -> 5.1 and 5.3 us).  A row's bits depend on this choice
+// only, so it is made per linear, as if the linear ran alone.
+static int lut_slots_for(int64_t n_gt, int k, int64_t n_rt) {
     int S = k <= 1 ? 1 : (k == 2 ? 2 : 4);
+    if (S == 4 && k <= 4) {
+        const int slices4 = lut_slices(n_gt, k, 4);
+        const int64_t rb = LUT_CUS / slices4 >= 1 ? LUT_CUS / slices4 : 1;
+        if ((n_rt + rb - 1) / rb < LUT_WAVES && lut_slices(n_gt, k, 2) <= LUT_MAX_SLICES) S = 2;
+    }
     while (S < 4 && lut_slices(n_gt, k, S) > LUT_MAX_SLICES) S *= 2;
     return S;
 }
@@ -403,13 +413,15 @@ static void launch_kl(int k, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) 
     }
 }
 
-// S = 1 only occurs at k = 1 and S = 2 only at k <= 2 (lut_slots_for), so only
+// S = 1 only occurs at k = 1 and S = 2 only at k <= 4 (lut_slots_for), so only
 // those instantiations exist.
 template <bool MULTI, int HB, int TPW>
 static void launch_k(int k, int S, dim3 gd, dim3 bd, hipStream_t s, const LutArgs& a) {
     if (S == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW, 1>), gd, bd, 0, s, AQD_LUT_ARGS);
     else if (S == 2 && k == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 1, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
-    else if (S == 2) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else if (S == 2 && k == 2) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 2, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else if (S == 2 && k == 3) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 3, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
+    else if (S == 2) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES, 4, MULTI, HB, TPW, 2>), gd, bd, 0, s, AQD_LUT_ARGS);
     else launch_kl<MULTI, HB, TPW, 4>(k, gd, bd, s, a);
 }
 #undef AQD_LUT_ARGS
@@ -420,8 +432,10 @@ static void launch_tpw(int tpw, int k, int S, dim3 gd, dim3 bd, hipStream_t s, c
     else launch_k<MULTI, HB, LUT_TILES_PER_WAVE>(k, S, gd, bd, s, a);
 }
 
-hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
-                                   void* ws, hipStream_t s, int rotate_block, const uint8_t* signs) {
+// One launch over linears that share S; acc[i] is linear i's counted row words.
+static hipError_t launch_lut_group(const LutLinearRef* lins, unsigned long long* const* acc, int n, int k, int S,
+                                   const uint16_t* x, int64_t d_in, hipStream_t s, int rotate_block,
+                                   const uint8_t* signs) {
     const int64_t G = d_in / GROUP;
     const int64_t n_gt = (G + TILE_GROUPS - 1) / TILE_GROUPS;
     LutArgs a = {};
@@ -431,48 +445,41 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
     a.n_gt = n_gt;
     a.k = k;
     a.n_slots = (int)((int64_t)k * n_gt);
-    const int S = lut_slots_for(n_gt, k);
     a.slices = lut_slices(n_gt, k, S);
     int64_t n_rt[LUT_MAX_GROUP];
     int tpb[LUT_MAX_GROUP], blocks[LUT_MAX_GROUP];
-    int m = 0;                                 // linears with rows
-    for (int i = 0; i < n; ++i)
-        if (lins[i].d_out > 0) {
-            a.lin[m].packed = lins[i].packed;
-            a.lin[m].codebooks = lins[i].codebooks;
-            a.lin[m].scales = lins[i].scales;
-            a.lin[m].y = lins[i].y;
-            a.lin[m].d_out = lins[i].d_out;
-            a.lin[m].n_rt = (lins[i].d_out + TILE_ROWS - 1) / TILE_ROWS;
-            a.lin[m].plane_bytes = a.lin[m].n_rt * n_gt * TILE_BYTES;
-            n_rt[m] = a.lin[m].n_rt;
-            ++m;
-        }
-    if (m == 0) return hipSuccess;
-    a.n_lin = m;
+    for (int i = 0; i < n; ++i) {
+        a.lin[i].packed = lins[i].packed;
+        a.lin[i].codebooks = lins[i].codebooks;
+        a.lin[i].scales = lins[i].scales;
+        a.lin[i].y = lins[i].y;
+        a.lin[i].acc = acc[i];
+        a.lin[i].d_out = lins[i].d_out;
+        a.lin[i].n_rt = (lins[i].d_out + TILE_ROWS - 1) / TILE_ROWS;
+        a.lin[i].plane_bytes = a.lin[i].n_rt * n_gt * TILE_BYTES;
+        n_rt[i] = a.lin[i].n_rt;
+    }
+    a.n_lin = n;
     // two row tiles per wave, or four when two would need more workgroups than CUs (a second round)
-    const bool round4 = m == 1 && rotate_block == 0;   // the plain single-linear GEMV
+    const bool round4 = n == 1 && rotate_block == 0;   // the plain single-linear GEMV
     int tpw = LUT_TILES_PER_WAVE;
-    lut_plan(n_rt, m, a.slices, tpw, tpb, blocks, round4);
+    lut_plan(n_rt, n, a.slices, tpw, tpb, blocks, round4);
     int64_t wgs = 0;
-    for (int i = 0; i < m; ++i) wgs += (int64_t)a.slices * blocks[i];
+    for (int i = 0; i < n; ++i) wgs += (int64_t)a.slices * blocks[i];
     if (wgs > LUT_CUS) {
         tpw = LUT_TILES_PER_WAVE_BIG;
-        lut_plan(n_rt, m, a.slices, tpw, tpb, blocks, round4);
+        lut_plan(n_rt, n, a.slices, tpw, tpb, blocks, round4);
     }
-    uint8_t* acc = static_cast<uint8_t*>(ws);
     int wg = 0;
-    for (int i = 0; i < m; ++i) {
+    for (int i = 0; i < n; ++i) {
         a.lin[i].tiles_per_block = tpb[i];
         a.lin[i].wg_begin = wg;
-        a.lin[i].acc = reinterpret_cast<unsigned long long*>(acc);
-        acc += acc_bytes(a.lin[i].d_out);
         wg += a.slices * blocks[i];
     }
     const dim3 gd((unsigned)wg), bd(64 * LUT_WAVES);
     // one linear: the instantiation that takes every field its first loads need from the preloaded
     // leading arguments
-    const bool one = m == 1;
+    const bool one = n == 1;
     if (rotate_block == 64) one ? launch_tpw<false, 64>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 64>(tpw, k, S, gd, bd, s, a);
     else if (rotate_block == 128)
         one ? launch_tpw<false, 128>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 128>(tpw, k, S, gd, bd, s, a);
@@ -480,6 +487,36 @@ hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const
         one ? launch_tpw<false, 256>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 256>(tpw, k, S, gd, bd, s, a);
     else one ? launch_tpw<false, 0>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 0>(tpw, k, S, gd, bd, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv_lut_grouped(const LutLinearRef* lins, int n, int k, const uint16_t* x, int64_t d_in,
+                                   void* ws, hipStream_t s, int rotate_block, const uint8_t* signs) {
+    const int64_t n_gt = (d_in / GROUP + TILE_GROUPS - 1) / TILE_GROUPS;
+    // each linear's row words sit at its place in the workspace, in argument order
+    unsigned long long* acc[LUT_MAX_GROUP];
+    int slots[LUT_MAX_GROUP];
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    for (int i = 0; i < n; ++i) {
+        acc[i] = reinterpret_cast<unsigned long long*>(w);
+        w += acc_bytes(lins[i].d_out);
+        slots[i] = lut_slots_for(n_gt, k, (lins[i].d_out + TILE_ROWS - 1) / TILE_ROWS);
+    }
+    // the linears that take the same slots per workgroup share one launch (all of them, in practice)
+    for (int S = 1; S <= LUT_SLOTS; S *= 2) {
+        LutLinearRef part[LUT_MAX_GROUP];
+        unsigned long long* part_acc[LUT_MAX_GROUP];
+        int m = 0;
+        for (int i = 0; i < n; ++i)
+            if (lins[i].d_out > 0 && slots[i] == S) {
+                part[m] = lins[i];
+                part_acc[m] = acc[i];
+                ++m;
+            }
+        if (m == 0) continue;
+        const hipError_t e = launch_lut_group(part, part_acc, m, k, S, x, d_in, s, rotate_block, signs);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_gemv_lut(const uint8_t* packed, const uint16_t* codebooks, const uint16_t* scales, int k,

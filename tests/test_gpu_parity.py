@@ -443,6 +443,7 @@ def test_graph_replay_matches_eager(orc):
     ([14336, 14336], 4096, 2),               # gate, up
     ([14336, 14336], 4096, 4),               # gate, up with four row tiles per wave (one round of workgroups)
     ([1000, 0, 33, 16], 1000, 2),            # ragged rows and groups, an empty linear, four linears
+    ([14336, 1024, 4096], 4096, 3),          # members that take 4 and 2 table slots: one launch per slot count
 ])
 def test_grouped_gemv_matches_separate_calls(orc, shapes, d_in, k):
     """One launch over several linears sharing the input gives, per linear, the bits of its own aqd_gemv
