@@ -223,7 +223,8 @@ def aqd_gemv_grouped_workspace_bytes(d_outs, d_in: int, Ms) -> int:
 def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
                      workspace: Optional[torch.Tensor] = None, block: int = 0,
                      signs: Optional[torch.Tensor] = None):
-    """Batch-1 GEMV of several linears sharing x_rot (fp16 [d_in] or [1][d_in]) in one launch.
+    """Batch-1 GEMV of several linears sharing x_rot (fp16 [d_in] or [1][d_in]) in one launch (one per
+    table-slot choice when the linears' sizes call for different ones; each output has its own call's bits).
 
     linears: sequence of (packed, codebooks, scales, d_out, M) or (packed, codebooks, scales, d_out, M, out);
     returns the fp16 outputs [1][d_out], one per linear.  With block (64/128/256) the input is the raw

@@ -242,7 +242,10 @@ aqd_status aqd_gemv_noalloc(const uint8_t* packed_codes, const uint16_t* codeboo
  * Grouped batch-1 GEMV: up to AQD_MAX_GROUP linears that read the same rotated
  * input (q, k and v of an attention block; gate and up of an MLP) in one
  * launch.  Each linear computes exactly what aqd_gemv computes for it at
- * batch 1 (Drop-by-Drop, sections 3.2 and 5), with the same bits.
+ * batch 1 (Drop-by-Drop, sections 3.2 and 5), with the same bits.  The table
+ * slots per workgroup, which decide the bits, are chosen per linear as for
+ * aqd_gemv; linears that choose differently (a small linear beside a large one
+ * at k = 3 or 4) are issued as one launch per choice, in the same stream.
  *
  * linears:   n_linears descriptors (host memory, read during the call only):
  *            packed codes, codebooks, scales and fp16 output y [d_out] of each
