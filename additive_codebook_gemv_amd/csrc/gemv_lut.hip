@@ -10,8 +10,9 @@
 //
 // Work split.  A "slot" is one (group tile, codebook) pair: 64 groups of one
 // plane.  A workgroup owns a slice of S consecutive slots (S = 1 at k = 1, 2 at
-// k = 2, 4 from k = 3; more if a row would otherwise take more than 255
-// contributions) and a block of row tiles.  It builds the S x 64 tables of its
+// k = 2, 4 from k = 3 except on linears too small to give each wave a row tile,
+// which keep 2; more if a row would otherwise take more than 255 contributions)
+// and a block of row tiles.  It builds the S x 64 tables of its
 // slice with matrix-core products (v_mfma_f32_32x32x8_f16: 32 codewords x 8
 // elements times 8 elements x 32 groups) and stores them as fp16 in LDS, then
 // streams its row tiles: lane l of a wave loads the 16 codes of group l for 16
