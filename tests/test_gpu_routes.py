@@ -8,7 +8,8 @@
 - the 32-layer stack exactly as the benchmark issues it: one launch per
   q/k/v group, o, gate/up group and down, each rotating its own input, every
   layer at its seeded k, checked per linear against the oracle on sampled rows;
-- the rotating grouped launch on every stack shape at k = 2, 3 and 4;
+- the rotating grouped launch on every stack shape at k = 2, 3 and 4, and on a group whose
+  members choose different table slots per workgroup;
 - the table paths (batch 1 and 2) over a sweep of activation and codebook
   magnitudes, since their fp16 table entries and fixed-point row sums have an
   absolute error floor.
@@ -125,6 +126,7 @@ def test_stack_fused_schedule_sampled(orc):
     ([4096], 4096, 128),                   # o: one linear that rotates its own input
     ([14336, 14336], 4096, 128),           # gate, up
     ([4096], 14336, 256),                  # down
+    ([14336, 1024], 4096, 128),            # members that take 4 and 2 table slots at k = 3, 4: two launches
 ])
 def test_rotating_launch_every_stack_shape_and_k(orc, shapes, d_in, block, k):
     g = wl.rng(621, extra=d_in + block + sum(shapes) + k)
