@@ -216,6 +216,28 @@ def test_gemv_edge_shapes(orc, d_out, d_in, M, batches):
             assert e <= TOL, (k, B, e)
 
 
+def test_gemv_tall_layer_many_rounds(orc):
+    """2^20 rows over 512 inputs: the batch-1, batch-2, four-column and matrix-core routes all plan
+    several rounds of workgroups (1024 or more for the table routes, with four row tiles per wave).
+    Sampled rows, the first and the last among them, against the oracle."""
+    d_out, d_in, M = 1 << 20, 512, 2
+    g = wl.rng(41, extra=d_out)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    x = wl.gen_x(g, 8, d_in, "f16")                      # stands for an already rotated activation
+    packed = aqd.aqd_pack_codes(to_dev(codes))
+    cbd, sd = to_dev(cb), to_dev(s)
+    pick = np.random.Generator(np.random.PCG64(42)).choice(d_out, size=254, replace=False)
+    rows = np.unique(np.concatenate([[0, d_out - 1], pick]))
+    for k in (1, 2):
+        ref = orc.linear(codes[rows], cb, s[rows], k, x)
+        for B in (1, 2, 4, 8):
+            y = aqd.aqd_gemv(packed, cbd, sd, k, to_dev(x[:B]), d_out, d_in, M).cpu().numpy()[:, rows]
+            e = normwise(y, ref[:B])
+            record(test="gemv_tall", shape=[d_out, d_in, M], k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
+    del packed
+
+
 def test_gemv_empty_input_gives_zero():
     d_out = 40
     s = to_dev(np.ones(d_out, dtype=np.float16))
