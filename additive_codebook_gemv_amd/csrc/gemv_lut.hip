@@ -233,11 +233,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     // built; the other tiles are requested after the build (below), so that
     // workgroups still waiting for their operands are not queued behind them.
     uint4 codes[TPW][S];
-    auto load_tile = [&](int u) {
+    auto load_slot = [&](int u, int s) {
         const int64_t it = t0 + wave + (int64_t)u * WAVES;
         const uint32_t off = it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE;
+        codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
+    };
+    auto load_tile = [&](int u) {
 #pragma unroll
-        for (int s = 0; s < S; ++s) codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
+        for (int s = 0; s < S; ++s) load_slot(u, s);
     };
     load_tile(0);
     if (HB > 0) {
@@ -290,8 +293,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         }
     }
     __syncthreads();
+    // with 2 or 4 slots, tile u + 1 is requested from inside tile u's lookups (below)
+    if constexpr (S == 1) {
 #pragma unroll
-    for (int u = 1; u < TPW; ++u) load_tile(u);
+        for (int u = 1; u < TPW; ++u) load_tile(u);
+    }
 
     const LutLinear L = p.lin[MULTI ? l : 0];
     // scales of the rows this lane may finish (needed only at the end; clamped)
@@ -322,18 +328,46 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         // per row quad q and slot pair: the entries (4 rows x the pair's slots) of this lane in the
         // fp16 halves of the B operand; one product routes them into D (lut_route)
         floatx4_t d = {0.f, 0.f, 0.f, 0.f};
+        // (row quad q, slot sl) pairs in q-major order; the zero-extended 2-byte reads are the B dwords
+        // (entry in the low half, zero above)
+        auto read_pair = [&](int n, uint32_t (&e)[4]) {
+            const int q = n / S, sl = n % S;
+            const uint4& c = codes[u][sl];
+            const uint32_t w = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+            for (int m = 0; m < 4; ++m) e[m] = *reinterpret_cast<const uint16_t*>(lds + lut_addr(w, base[sl], m));
+        };
+        constexpr int NP = 4 * S;
+        if constexpr (S == 1) {
 #pragma unroll
-            for (int sl = 0; sl < S; ++sl) {
-                const uint4& c = codes[u][sl];
-                const uint32_t w = q == 0 ? c.x : q == 1 ? c.y : q == 2 ? c.z : c.w;
-                // the zero-extended 2-byte reads are the B dwords: entry in the low half, zero above
+            for (int n = 0; n < NP; ++n) {
                 uint32_t e[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) e[m] = *reinterpret_cast<const uint16_t*>(lds + lut_addr(w, base[sl], m));
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[q], __builtin_bit_cast(half8_t, make_uint4(e[0], e[1], e[2], e[3])),
+                read_pair(n, e);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[n], __builtin_bit_cast(half8_t, make_uint4(e[0], e[1], e[2], e[3])),
                                                            d, 0, 0, 0);
+            }
+        } else {
+            // Software pipeline: the reads of pair n + LA go out before the product of pair n (the
+            // scheduling barriers keep that order), so a wave keeps 8 reads in flight instead of
+            // draining them every two products; same products in the same order.  The next tile's
+            // slots are requested from here, half after 3/8 and half after 11/16 of the products.
+            constexpr int LA = 2;
+            uint32_t e[LA + 1][4];
+#pragma unroll
+            for (int n = 0; n < LA; ++n) read_pair(n, e[n]);
+#pragma unroll
+            for (int n = 0; n < NP; ++n) {
+                if (n + LA < NP) read_pair(n + LA, e[(n + LA) % (LA + 1)]);
+                __builtin_amdgcn_sched_barrier(0);
+                const uint32_t (&cur)[4] = e[n % (LA + 1)];
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[n / S],
+                                                           __builtin_bit_cast(half8_t, make_uint4(cur[0], cur[1], cur[2], cur[3])), d, 0, 0, 0);
+                if (u + 1 < TPW) {
+#pragma unroll
+                    for (int sl = 0; sl < S; ++sl)
+                        if (n == (sl < (S + 1) / 2 ? (6 * NP) / 16 : (11 * NP) / 16)) load_slot(u + 1, sl);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         const float sum = fold_quads(d, lane);
