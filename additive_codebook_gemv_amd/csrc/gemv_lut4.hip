@@ -20,7 +20,9 @@
 // accumulator a in lanes 4i .. 4i+3, and lane 4i + a adds it through the
 // counted fixed-point word of its (column, row) (batch 1): one atomic
 // instruction per tile serves all 64 sums.  With three columns the fourth is
-// computed from a zero activation and not stored.
+// computed from a zero activation and not stored.  The reads of a product go
+// out two products ahead (a software pipeline held in order by scheduling
+// barriers), as in the batch-1 kernel.
 #include "lut_device.h"
 
 namespace aqd {
@@ -141,17 +143,27 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
         if (it >= t1) break;                    // uniform across the wave
         floatx4_t d[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            d[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < 4; ++q) d[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        // (q, pr) pairs: the (column 0..3) entries of rows 4q + 2pr and 4q + 2pr + 1; pair n + 2's reads
+        // go out before pair n's product
+        auto read_pair = [&](int n, uint4& v) {
+            const int q = n >> 1, pr = n & 1;
             const uint32_t w = q == 0 ? codes[u].x : q == 1 ? codes[u].y : q == 2 ? codes[u].z : codes[u].w;
+            const uint2 e = *reinterpret_cast<const uint2*>(lds + 2 * lut_addr(w, base, 2 * pr));
+            const uint2 f = *reinterpret_cast<const uint2*>(lds + 2 * lut_addr(w, base, 2 * pr + 1));
+            v = make_uint4(e.x, e.y, f.x, f.y);
+        };
+        constexpr int NP = 8, LA = 2;
+        uint4 ev[LA + 1];
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                // (column 0..3) entries of rows 4q + 2pr and 4q + 2pr + 1
-                const uint2 e = *reinterpret_cast<const uint2*>(lds + 2 * lut_addr(w, base, 2 * pr));
-                const uint2 f = *reinterpret_cast<const uint2*>(lds + 2 * lut_addr(w, base, 2 * pr + 1));
-                d[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    route[pr], __builtin_bit_cast(half8_t, make_uint4(e.x, e.y, f.x, f.y)), d[q], 0, 0, 0);
-            }
+        for (int n = 0; n < LA; ++n) read_pair(n, ev[n]);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            if (n + LA < NP) read_pair(n + LA, ev[(n + LA) % (LA + 1)]);
+            __builtin_amdgcn_sched_barrier(0);
+            d[n >> 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(route[n & 1], __builtin_bit_cast(half8_t, ev[n % (LA + 1)]),
+                                                               d[n >> 1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
         float sq[4];
 #pragma unroll
