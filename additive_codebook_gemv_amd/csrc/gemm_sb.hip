@@ -5,11 +5,12 @@
 // but with enough activation columns that the work is a dense contraction:
 //     Y[n][i] = s_i * sum_c W_k[i][c] * X[n][c].
 //
-// Workgroup: 8 waves, one 16-row tile each (128 rows), all batch columns, a
-// range of 128-input chunks (the input dimension is split over gridDim.y).
+// Workgroup: 8 waves (7 where that spreads the row tiles more evenly over the
+// CUs, see sb_plan), one 16-row tile each, all batch columns, a range of
+// 128-input chunks (the input dimension is split over gridDim.y).
 // Per chunk:
 //   - the rotated activation chunk (batch x 128) is staged once in LDS, double
-//     buffered, and shared by the 8 waves (MFMA B operands, padded rows so the
+//     buffered, and shared by the waves (MFMA B operands, padded rows so the
 //     16-byte reads do not collide);
 //   - each lane rebuilds exactly the 8 weights its MFMA A-operand slot holds:
 //     it gathers the k codewords of its (row, group) from the LDS-resident
@@ -30,7 +31,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int SB_WAVES = 8;
+constexpr int SB_WAVES = 8;                        // waves per workgroup at most
+constexpr int SB_MIN_WAVES = 7;                    // and at least
 constexpr int SB_CHUNK = 128;                      // inputs per chunk (16 groups)
 constexpr int SB_CHUNK_GROUPS = SB_CHUNK / GROUP;
 constexpr int SB_XROW = SB_CHUNK * 2 + 16;         // bytes per activation row in LDS (padded)
@@ -67,8 +69,8 @@ __device__ __forceinline__ void split_bf16(uint32_t h, uint32_t& hi, uint32_t& l
     lo = __builtin_bit_cast(uint32_t, lv);
 }
 
-template <int NT, int MODE, int K>
-__global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
+template <int NT, int MODE, int K, int W>
+__global__ __launch_bounds__(64 * W) void gemm_sb_kernel(
     const uint8_t* __restrict__ packed, const uint4* __restrict__ codebooks, const uint16_t* __restrict__ scales,
     const uint16_t* __restrict__ x, float* __restrict__ out, int64_t d_out, int64_t d_in, int64_t G,
     int64_t n_rt, int64_t plane_bytes, int batch, int chunks_per_split, int64_t n_chunks, int direct,
@@ -82,14 +84,15 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t it = (int64_t)blockIdx.x * SB_WAVES + wave;            // this wave's row tile
+    constexpr int nthreads = 64 * W;
+    const int64_t it = (int64_t)blockIdx.x * W + wave;            // this wave's row tile
     const bool row_ok = it < n_rt;
     const int64_t c0 = (int64_t)blockIdx.y * chunks_per_split;
     const int64_t c1 = c0 + chunks_per_split < n_chunks ? c0 + chunks_per_split : n_chunks;
     const int r = lane & 15;      // MFMA A row (weight row in the tile) / B column in the tile
     const int kq = lane >> 4;     // 8-wide k slot inside the 32-wide MFMA step
 
-    for (int i = tid; i < K * CODEWORDS; i += 64 * SB_WAVES) cb_lds[i] = codebooks[i];
+    for (int i = tid; i < K * CODEWORDS; i += nthreads) cb_lds[i] = codebooks[i];
     // tiered batch: the codebooks each of this lane's B columns uses (bit m)
     uint32_t col_planes[NT];
 #pragma unroll
@@ -101,13 +104,13 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
 
     // activation chunk staging: thread t moves 16 bytes (8 inputs) of one row of one plane
     constexpr int X_ITEMS = XP * NT * 16 * (SB_CHUNK / 8);   // 16-byte pieces per chunk
-    constexpr int X_PER_THREAD = (X_ITEMS + 64 * SB_WAVES - 1) / (64 * SB_WAVES);
+    constexpr int X_PER_THREAD = (X_ITEMS + nthreads - 1) / nthreads;
     // every load is issued unconditionally (addresses clamped into the buffer, out-of-range pieces zeroed
     // afterwards), so the loads of the next chunk stay in flight while this chunk is multiplied
     auto x_load = [&](int64_t ch, uint4 (&v)[X_PER_THREAD]) {
 #pragma unroll
         for (int q = 0; q < X_PER_THREAD; ++q) {
-            const int item = (tid + q * 64 * SB_WAVES) % X_ITEMS;
+            const int item = (tid + q * nthreads) % X_ITEMS;
             const int piece = item % (SB_CHUNK / 8);
             const int col = (item / (SB_CHUNK / 8)) % (NT * 16);
             const int pl = item / ((SB_CHUNK / 8) * NT * 16);
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     auto x_fix = [&](int64_t ch, uint4 (&v)[X_PER_THREAD]) {
 #pragma unroll
         for (int q = 0; q < X_PER_THREAD; ++q) {
-            const int item = (tid + q * 64 * SB_WAVES) % X_ITEMS;
+            const int item = (tid + q * nthreads) % X_ITEMS;
             const int piece = item % (SB_CHUNK / 8);
             const int col = (item / (SB_CHUNK / 8)) % (NT * 16);
             if (col >= batch || ch * SB_CHUNK + piece * 8 >= d_in) v[q] = make_uint4(0u, 0u, 0u, 0u);
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(64 * SB_WAVES) void gemm_sb_kernel(
     auto x_store = [&](int buf, const uint4 (&v)[X_PER_THREAD]) {
 #pragma unroll
         for (int q = 0; q < X_PER_THREAD; ++q) {
-            const int item = tid + q * 64 * SB_WAVES;
+            const int item = tid + q * nthreads;
             if (item < X_ITEMS) {
                 const int piece = item % (SB_CHUNK / 8);
                 const int row = item / (SB_CHUNK / 8);          // pl * NT*16 + col
@@ -361,7 +364,7 @@ constexpr size_t sb_lds_bytes(int k, int nt) {
 
 struct SbPlan {
     int64_t n_chunks, wg_rows;
-    int splits, chunks_per_split;
+    int splits, chunks_per_split, waves;
 };
 
 // Splits of the input dimension: the smallest split count that minimises
@@ -370,6 +373,7 @@ struct SbPlan {
 static SbPlan sb_plan(const Geometry& g, int per_cu) {
     SbPlan p;
     p.n_chunks = (g.d_in + SB_CHUNK - 1) / SB_CHUNK;
+    p.waves = SB_WAVES;
     p.wg_rows = (g.n_rt + SB_WAVES - 1) / SB_WAVES;
     p.splits = 1;
     p.chunks_per_split = (int)p.n_chunks;
@@ -386,11 +390,21 @@ static SbPlan sb_plan(const Geometry& g, int per_cu) {
             p.chunks_per_split = (int)cps;
         }
     }
+    // With 8-wave workgroups the busiest CU may hold one more workgroup than the others.  Workgroups of
+    // 7 waves (same splits, so the same sums) are taken when they fit one round and leave the busiest CU
+    // fewer row tiles.
+    const int64_t wgs8 = p.wg_rows * p.splits;
+    const int64_t rows7 = (g.n_rt + SB_MIN_WAVES - 1) / SB_MIN_WAVES;
+    const int64_t wgs7 = rows7 * p.splits;
+    if (wgs7 <= slots && ((wgs7 + 255) / 256) * SB_MIN_WAVES < ((wgs8 + 255) / 256) * SB_WAVES) {
+        p.waves = SB_MIN_WAVES;
+        p.wg_rows = rows7;
+    }
     return p;
 }
 
-// Workgroups of 8 waves resident per CU: bounded by the LDS the batch tile needs
-// (VGPR use, about 128 per lane, allows two).
+// Workgroups of 7 or 8 waves resident per CU: bounded by the LDS the batch tile
+// needs (VGPR use, at most 128 per lane, allows two).
 template <int MODE>
 static int sb_per_cu(int k, int batch) {
     const size_t lds = sb_lds_bytes<MODE>(k, (batch + 15) / 16);
@@ -427,12 +441,17 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                                         : launch_zero_f32(y, n, s);   // empty input: Y = 0
     const bool direct = p.splits == 1;
     constexpr size_t lds = sb_lds_bytes<MODE>(K, NT);
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)lds);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_sb_kernel<NT, MODE, K>), dim3((unsigned)p.wg_rows, (unsigned)p.splits),
-                       dim3(64 * SB_WAVES), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
+    static const hipError_t attr8 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_WAVES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static const hipError_t attr7 = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr8 != hipSuccess) return attr8;
+    if (attr7 != hipSuccess) return attr7;
+    auto kern = p.waves == SB_MIN_WAVES ? &gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES> : &gemm_sb_kernel<NT, MODE, K, SB_WAVES>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.wg_rows, (unsigned)p.splits),
+                       dim3(64 * p.waves), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
                        direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
                        p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
     hipError_t e = hipGetLastError();
