@@ -13,6 +13,9 @@
 - the table paths (batch 1 and 2) over a sweep of activation and codebook
   magnitudes, since their fp16 table entries and fixed-point row sums have an
   absolute error floor.
+- the small-batch kernel in its 7-wave form on a layer whose row tiles do not
+  fill the last workgroup (14320 rows: 895 tiles in 128 workgroups of 7), as
+  the small-batch call and as the matrix-core route of the batch-8 GEMV.
 
 Every comparison is against the fp64 oracle (Drop-by-Drop, section 3.2: the
 group sums of the first k codebooks; section 5: the block rotation applied to
@@ -59,6 +62,27 @@ def test_quantized_linear_batch_sequence(orc):
         assert e <= TOL, (step, B, k, e)
         if B <= 4:
             assert torch.count_nonzero(q.workspace[:n1]).item() == 0, (step, B)
+
+
+def test_small_batch_seven_wave_ragged(orc):
+    """14320 x 4096 plans 7-wave workgroups (4 input splits: 112 eight-wave row blocks would leave 64 CUs
+    with one workgroup and the rest with two); the last workgroup holds 6 row tiles and one idle wave."""
+    d_out, d_in, M = 14320, 4096, 4
+    g = wl.rng(621)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    xr = wl.gen_x(g, 40, d_in, "f16")                    # stands for an already rotated activation
+    packed, cbd, sd = _upload(codes, cb, s)
+    for k in (2, 4):
+        ref = orc.linear(codes, cb, s, k, xr)
+        for B in (16, 40):
+            y = aqd.aqd_gemm_small_batch(packed, cbd, sd, k, to_dev(xr[:B]), d_out, d_in, M, aqd.AQD_F16)
+            e = normwise(y.cpu().numpy(), ref[:B])
+            record(test="small_batch_seven_wave", k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
+        y8 = aqd.aqd_gemv(packed, cbd, sd, k, to_dev(xr[:8]), d_out, d_in, M).float().cpu().numpy()
+        e8 = normwise(y8, ref[:8])
+        record(test="gemv_batch8_seven_wave", k=k, err=e8)
+        assert e8 <= TOL, (k, e8)
 
 
 @pytest.mark.parametrize("d_out,d_in,M,batches", [
