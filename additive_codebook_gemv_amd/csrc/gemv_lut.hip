@@ -9,12 +9,13 @@
 // 16-byte codeword gather and four dot2 steps.
 //
 // Work split.  A "slot" is one (group tile, codebook) pair: 64 groups of one
-// plane.  A workgroup owns a slice of S consecutive slots (S = 1 at k = 1, 2 at
-// k = 2, 4 from k = 3 except on linears too small to give each wave a row tile,
-// which keep 2; more if a row would otherwise take more than 255 contributions)
-// and a block of row tiles.  It builds the S x 64 tables of its
-// slice with matrix-core products (v_mfma_f32_32x32x8_f16: 32 codewords x 8
-// elements times 8 elements x 32 groups) and stores them as fp16 in LDS, then
+// plane.  A workgroup owns a slice of S consecutive slots (S = 1 at k = 1 on
+// inputs under 6144, else 2 at k <= 2, 4 from k = 3 except on linears too
+// small to give each wave a row tile, which keep 2; more if a row would
+// otherwise take more than 255 contributions) and a block of row tiles.  It
+// builds the S x 64 tables of its slice with matrix-core products
+// (v_mfma_f32_32x32x8_f16: 32 codewords x 8 elements times 8 elements x 32
+// groups) and stores them as fp16 in LDS, then
 // streams its row tiles: lane l of a wave loads the 16 codes of group l for 16
 // rows for each slot (one coalesced 1 KiB tile per slot) and looks up the
 // table entry of every row and slot.  A slot's tables cost the same to build
@@ -414,14 +415,18 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
 }
 
 // Slots per workgroup for one linear: as many as k (1, 2, then 4), more when
-// the slices would exceed what a row's counted sum allows.  With 4 slots, a
+// the slices would exceed what a row's counted sum allows.  At k = 1 an input
+// of 12 or more group tiles (6144 inputs) takes 2: half the slices, so each
+// row takes half the counted adds and a tall layer fits one round of
+// workgroups (4096x14336 5.3 -> 4.9 us, 14336x14336 13.0 -> 8.3 us; at 5120
+// inputs even, at 4096 one slot is 0.1-0.2 us faster).  With 4 slots, a
 // linear too small to give every wave of a workgroup a row tile (fewer tiles
 // per workgroup than waves) takes 2: the 4-slot table build would otherwise
 // sit on the critical path of half-idle workgroups (measured on 4096x4096 at
 // k = 3 and 4: 5.9 -> 5.1 and 5.3 us).  A row's bits depend on this choice
 // only, so it is made per linear, as if the linear ran alone.
 static int lut_slots_for(int64_t n_gt, int k, int64_t n_rt) {
-    int S = k <= 1 ? 1 : (k == 2 ? 2 : 4);
+    int S = k <= 1 ? (n_gt >= 12 ? 2 : 1) : (k == 2 ? 2 : 4);
     if (S == 4 && k <= 4) {
         const int slices4 = lut_slices(n_gt, k, 4);
         const int64_t rb = LUT_CUS / slices4 >= 1 ? LUT_CUS / slices4 : 1;
