@@ -416,9 +416,9 @@ size_t gemv_lut_grouped_workspace_bytes(const int64_t* d_out, int n) {
 
 // Slots per workgroup for one linear: as many as k (1, 2, then 4), more when
 // the slices would exceed what a row's counted sum allows.  At k = 1 an input
-// of 12 or more group tiles (6144 inputs) takes 2: half the slices, so each
-// row takes half the counted adds and a tall layer fits one round of
-// workgroups (4096x14336 5.3 -> 4.9 us, 14336x14336 13.0 -> 8.3 us; at 5120
+// of 12 or more group tiles (6144 inputs) takes 2: half the slices, one row
+// tile per wave on 4096 rows instead of two, and a tall layer fits one round
+// of workgroups (4096x14336 5.3 -> 4.9 us, 14336x14336 13.0 -> 8.3 us; at 5120
 // inputs even, at 4096 one slot is 0.1-0.2 us faster).  With 4 slots, a
 // linear too small to give every wave of a workgroup a row tile (fewer tiles
 // per workgroup than waves) takes 2: the 4-slot table build would otherwise
