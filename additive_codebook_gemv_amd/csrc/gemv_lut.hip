@@ -11,7 +11,8 @@
 // Work split.  A "slot" is one (group tile, codebook) pair: 64 groups of one
 // plane.  A workgroup owns a slice of S consecutive slots (S = 1 at k = 1 on
 // inputs under 6144, else 2 at k <= 2, 4 from k = 3 except on linears too
-// small to give each wave a row tile, which keep 2; more if a row would
+// small to give each wave a row tile and, at k = 3, on long inputs whose
+// 2-slot plan fits one round of workgroups, which keep 2; more if a row would
 // otherwise take more than 255 contributions) and a block of row tiles.  It
 // builds the S x 64 tables of its slice with matrix-core products
 // (v_mfma_f32_32x32x8_f16: 32 codewords x 8 elements times 8 elements x 32
@@ -431,6 +432,14 @@ static int lut_slots_for(int64_t n_gt, int k, int64_t n_rt) {
         const int slices4 = lut_slices(n_gt, k, 4);
         const int64_t rb = LUT_CUS / slices4 >= 1 ? LUT_CUS / slices4 : 1;
         if ((n_rt + rb - 1) / rb < LUT_WAVES && lut_slices(n_gt, k, 2) <= LUT_MAX_SLICES) S = 2;
+    }
+    // k = 3 on long inputs: 2 slots when that plan still fits one round of workgroups (with four row
+    // tiles per wave).  4096x14336 8.1 -> 7.7 us; where it would need a second round (8192x14336) it is
+    // far slower, and at k = 4 the same rule was mixed (4096x14336 9.1 -> 9.7 us), so k = 4 keeps 4.
+    if (k == 3 && S == 4 && n_gt >= 16) {
+        const int sl2 = lut_slices(n_gt, k, 2);
+        const int64_t per_wg = (int64_t)LUT_WAVES * LUT_TILES_PER_WAVE_BIG;
+        if (sl2 <= LUT_MAX_SLICES && (n_rt + per_wg - 1) / per_wg * sl2 <= LUT_CUS) S = 2;
     }
     while (S < 4 && lut_slices(n_gt, k, S) > LUT_MAX_SLICES) S *= 2;
     return S;
