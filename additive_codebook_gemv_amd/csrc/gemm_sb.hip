@@ -6,8 +6,9 @@
 //     Y[n][i] = s_i * sum_c W_k[i][c] * X[n][c].
 //
 // Workgroup: 8 waves (7 where that spreads the row tiles more evenly over the
-// CUs, see sb_plan), one 16-row tile each, all batch columns, a range of
-// 128-input chunks (the input dimension is split over gridDim.y).
+// CUs, see sb_plan; 16 where the LDS holds only one workgroup per CU), one
+// 16-row tile each, all batch columns, a range of 128-input chunks (the input
+// dimension is split over gridDim.y).
 // Per chunk:
 //   - the rotated activation chunk (batch x 128) is staged once in LDS, double
 //     buffered, and shared by the waves (MFMA B operands, padded rows so the
@@ -33,6 +34,7 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr int SB_WAVES = 8;                        // waves per workgroup at most
 constexpr int SB_MIN_WAVES = 7;                    // and at least
+constexpr int SB_WIDE_WAVES = 16;                  // when the LDS allows one workgroup per CU
 constexpr int SB_CHUNK = 128;                      // inputs per chunk (16 groups)
 constexpr int SB_CHUNK_GROUPS = SB_CHUNK / GROUP;
 constexpr int SB_XROW = SB_CHUNK * 2 + 16;         // bytes per activation row in LDS (padded)
@@ -373,8 +375,8 @@ struct SbPlan {
 static SbPlan sb_plan(const Geometry& g, int per_cu) {
     SbPlan p;
     p.n_chunks = (g.d_in + SB_CHUNK - 1) / SB_CHUNK;
-    p.waves = SB_WAVES;
-    p.wg_rows = (g.n_rt + SB_WAVES - 1) / SB_WAVES;
+    p.waves = per_cu == 1 ? SB_WIDE_WAVES : SB_WAVES;
+    p.wg_rows = (g.n_rt + p.waves - 1) / p.waves;
     p.splits = 1;
     p.chunks_per_split = (int)p.n_chunks;
     if (p.wg_rows == 0 || p.n_chunks == 0) return p;
@@ -396,15 +398,16 @@ static SbPlan sb_plan(const Geometry& g, int per_cu) {
     const int64_t wgs8 = p.wg_rows * p.splits;
     const int64_t rows7 = (g.n_rt + SB_MIN_WAVES - 1) / SB_MIN_WAVES;
     const int64_t wgs7 = rows7 * p.splits;
-    if (wgs7 <= slots && ((wgs7 + 255) / 256) * SB_MIN_WAVES < ((wgs8 + 255) / 256) * SB_WAVES) {
+    if (p.waves == SB_WAVES && wgs7 <= slots && ((wgs7 + 255) / 256) * SB_MIN_WAVES < ((wgs8 + 255) / 256) * SB_WAVES) {
         p.waves = SB_MIN_WAVES;
         p.wg_rows = rows7;
     }
     return p;
 }
 
-// Workgroups of 7 or 8 waves resident per CU: bounded by the LDS the batch tile
-// needs (VGPR use, at most 128 per lane, allows two).
+// Workgroups resident per CU: bounded by the LDS the batch tile needs (VGPR
+// use, at most 128 per lane, allows two of 7 or 8 waves).  Where only one fits,
+// it has 16 waves.
 template <int MODE>
 static int sb_per_cu(int k, int batch) {
     const size_t lds = sb_lds_bytes<MODE>(k, (batch + 15) / 16);
@@ -441,19 +444,33 @@ static hipError_t launch_t(const uint8_t* packed, const uint16_t* cb, const uint
                                         : launch_zero_f32(y, n, s);   // empty input: Y = 0
     const bool direct = p.splits == 1;
     constexpr size_t lds = sb_lds_bytes<MODE>(K, NT);
-    static const hipError_t attr8 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_WAVES>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    static const hipError_t attr7 = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (attr8 != hipSuccess) return attr8;
-    if (attr7 != hipSuccess) return attr7;
-    auto kern = p.waves == SB_MIN_WAVES ? &gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES> : &gemm_sb_kernel<NT, MODE, K, SB_WAVES>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.wg_rows, (unsigned)p.splits),
-                       dim3(64 * p.waves), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
-                       direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
-                       p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
+    if constexpr (2 * lds > 160 * 1024) {
+        // one workgroup per CU fits the LDS: 16 waves, so the CU still holds 16
+        static const hipError_t attr16 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_WIDE_WAVES>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr16 != hipSuccess) return attr16;
+        if (p.waves != SB_WIDE_WAVES) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((gemm_sb_kernel<NT, MODE, K, SB_WIDE_WAVES>), dim3((unsigned)p.wg_rows, (unsigned)p.splits),
+                           dim3(64 * p.waves), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
+                           direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
+                           p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
+    } else {
+        static const hipError_t attr8 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_WAVES>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        static const hipError_t attr7 = hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr8 != hipSuccess) return attr8;
+        if (attr7 != hipSuccess) return attr7;
+        auto kern = p.waves == SB_MIN_WAVES ? &gemm_sb_kernel<NT, MODE, K, SB_MIN_WAVES>
+                                            : &gemm_sb_kernel<NT, MODE, K, SB_WAVES>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)p.wg_rows, (unsigned)p.splits),
+                           dim3(64 * p.waves), lds, s, packed, reinterpret_cast<const uint4*>(cb), scales, x,
+                           direct ? y : static_cast<float*>(ws), g.d_out, g.d_in, g.G, g.n_rt, g.plane_bytes, batch,
+                           p.chunks_per_split, p.n_chunks, direct ? 1 : 0, pc, out_f16);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || direct) return e;
     hipLaunchKernelGGL(sb_reduce_kernel,

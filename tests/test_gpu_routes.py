@@ -16,6 +16,8 @@
 - the small-batch kernel in its 7-wave form on a layer whose row tiles do not
   fill the last workgroup (14320 rows: 895 tiles in 128 workgroups of 7), as
   the small-batch call and as the matrix-core route of the batch-8 GEMV.
+- the small-batch kernel in its 16-wave form (bf16 hi + lo operands, k = 4,
+  49..64 columns: the LDS holds one workgroup per CU) on ragged rows.
 
 Every comparison is against the fp64 oracle (Drop-by-Drop, section 3.2: the
 group sums of the first k codebooks; section 5: the block rotation applied to
@@ -83,6 +85,28 @@ def test_small_batch_seven_wave_ragged(orc):
         e8 = normwise(y8, ref[:8])
         record(test="gemv_batch8_seven_wave", k=k, err=e8)
         assert e8 <= TOL, (k, e8)
+
+
+def test_small_batch_sixteen_wave_ragged(orc):
+    """1000 x 4096 with bf16 hi + lo activations at 49 and 64 columns, k = 4: 63 row tiles in workgroups
+    of 16 waves, the last one with 15 tiles and an idle wave."""
+    d_out, d_in, M = 1000, 4096, 4
+    g = wl.rng(631)
+    codes, cb, s = wl.gen_codes(g, d_out, d_in, M), wl.gen_codebooks(g, M), wl.gen_scales(g, d_out)
+    x = g.standard_normal((64, d_in)).astype(np.float32)   # stands for an already rotated activation
+    hi = torch.from_numpy(x).bfloat16()
+    lo = (torch.from_numpy(x) - hi.float()).bfloat16()
+    xd = torch.stack([hi, lo]).to(dev())
+    xr = (hi.float() + lo.float()).numpy().astype(np.float64)
+    packed, cbd, sd = _upload(codes, cb, s)
+    for k in (3, 4):
+        ref = orc.linear(codes, cb, s, k, xr)
+        for B in (49, 64):
+            y = aqd.aqd_gemm_small_batch(packed, cbd, sd, k, xd[:, :B].contiguous(), d_out, d_in, M,
+                                         aqd.AQD_BF16X2)
+            e = normwise(y.cpu().numpy(), ref[:B])
+            record(test="small_batch_sixteen_wave", k=k, batch=B, err=e)
+            assert e <= TOL, (k, B, e)
 
 
 @pytest.mark.parametrize("d_out,d_in,M,batches", [
