@@ -381,9 +381,11 @@ struct SbPlan {
     int splits, chunks_per_split, waves;
 };
 
-// Splits of the input dimension: the smallest split count that minimises
-// (rounds of workgroups over the chip) x (chunks per split), with `per_cu`
-// workgroups resident per compute unit; at most SB_MAX_SPLITS.
+// Waves per workgroup and splits of the input dimension.  Waves: 16 when the
+// LDS holds one workgroup per CU (per_cu == 1), else 8, or 7 where that evens
+// out the CUs (below).  Splits: the smallest count that minimises (rounds of
+// workgroups over the chip) x (chunks per split), with `per_cu` workgroups
+// resident per compute unit; at most SB_MAX_SPLITS.
 static SbPlan sb_plan(const Geometry& g, int per_cu) {
     SbPlan p;
     p.n_chunks = (g.d_in + SB_CHUNK - 1) / SB_CHUNK;
