@@ -481,6 +481,24 @@ static void launch_tpw(int tpw, int k, int S, dim3 gd, dim3 bd, hipStream_t s, c
     else launch_k<MULTI, HB, LUT_TILES_PER_WAVE>(k, S, gd, bd, s, a);
 }
 
+// Single-linear launches whose plan leaves at most 8 row tiles per workgroup (S <= 2, two tiles per
+// wave): the same plan in 8-wave workgroups.  Every tile and sum is as in the 16-wave launch, so are the
+// bits; half the waves to launch and to wait for at the table barrier (4096x4096 k = 1 / 2: 3.78 / 4.26
+// -> 3.57 / 3.97 us; 1024 and 2048 rows alike).
+#define AQD_LUT_ARGS8 a.lin[0].packed, a.lin[0].codebooks, a.x, a.lin[0].plane_bytes, (int)a.lin[0].n_rt, \
+                      (int)a.G, a.slices, a.n_slots, a.lin[0].tiles_per_block, a
+template <int HB>
+static void launch_w8(int k, int S, dim3 gd, hipStream_t s, const LutArgs& a) {
+    const dim3 bd(64 * LUT_WAVES_SMALL);
+    constexpr int T = LUT_TILES_PER_WAVE;
+    if (S == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES_SMALL, 1, false, HB, T, 1>), gd, bd, 0, s, AQD_LUT_ARGS8);
+    else if (k == 1) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES_SMALL, 1, false, HB, T, 2>), gd, bd, 0, s, AQD_LUT_ARGS8);
+    else if (k == 2) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES_SMALL, 2, false, HB, T, 2>), gd, bd, 0, s, AQD_LUT_ARGS8);
+    else if (k == 3) hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES_SMALL, 3, false, HB, T, 2>), gd, bd, 0, s, AQD_LUT_ARGS8);
+    else hipLaunchKernelGGL((gemv_lut_kernel<LUT_WAVES_SMALL, 4, false, HB, T, 2>), gd, bd, 0, s, AQD_LUT_ARGS8);
+}
+#undef AQD_LUT_ARGS8
+
 // One launch over linears that share S; acc[i] is linear i's counted row words.
 static hipError_t launch_lut_group(const LutLinearRef* lins, unsigned long long* const* acc, int n, int k, int S,
                                    const uint16_t* x, int64_t d_in, hipStream_t s, int rotate_block,
@@ -529,6 +547,13 @@ static hipError_t launch_lut_group(const LutLinearRef* lins, unsigned long long*
     // one linear: the instantiation that takes every field its first loads need from the preloaded
     // leading arguments
     const bool one = n == 1;
+    if (one && tpw == LUT_TILES_PER_WAVE && S <= 2 && k <= 4 && tpb[0] <= LUT_WAVES_SMALL) {
+        if (rotate_block == 64) launch_w8<64>(k, S, gd, s, a);
+        else if (rotate_block == 128) launch_w8<128>(k, S, gd, s, a);
+        else if (rotate_block == 256) launch_w8<256>(k, S, gd, s, a);
+        else launch_w8<0>(k, S, gd, s, a);
+        return hipGetLastError();
+    }
     if (rotate_block == 64) one ? launch_tpw<false, 64>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 64>(tpw, k, S, gd, bd, s, a);
     else if (rotate_block == 128)
         one ? launch_tpw<false, 128>(tpw, k, S, gd, bd, s, a) : launch_tpw<true, 128>(tpw, k, S, gd, bd, s, a);

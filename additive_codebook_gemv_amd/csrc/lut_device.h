@@ -18,6 +18,7 @@ constexpr int LUT_PAIR_BYTES = CODEWORDS * 64 * 4;           // 64 KiB
 constexpr int LUT_BYTES = (LUT_SLOTS / 2) * LUT_PAIR_BYTES;  // 128 KiB
 constexpr int LUT_CUS = 256;                                  // one 128 KiB workgroup per CU
 constexpr int LUT_WAVES = 16;
+constexpr int LUT_WAVES_SMALL = 8;                            // waves of a workgroup with at most 8 row tiles
 constexpr int LUT_TILES_PER_WAVE = 2;                         // row tiles per wave, default
 constexpr int LUT_TILES_PER_WAVE_BIG = 4;                     // ... when 2 would need more workgroups than CUs
 
