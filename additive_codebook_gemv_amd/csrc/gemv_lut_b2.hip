@@ -45,8 +45,8 @@ struct Lut2Args {
     int k, n_slots, slices, tiles_per_block;
 };
 
-template <int K, int TPW>
-__global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
+template <int K, int TPW, int W = LUT_WAVES>
+__global__ __launch_bounds__(64 * W) void gemv_lut2_kernel(Lut2Args p) {
     __shared__ __align__(16) uint8_t lds[LUT_BYTES];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -72,12 +72,12 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
 
     // ---- table operands.  Item = (slot, block of 32 codewords, block of 32
     // groups); its two products are the two columns.
-    constexpr int ITEMS = 32 / LUT_WAVES;
+    constexpr int ITEMS = 32 / W;
     uint2 av[ITEMS], bv[ITEMS][2];
     bool bok[ITEMS];
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
-        const int item = wave + u * LUT_WAVES;
+        const int item = wave + u * W;
         const int s = item >> 4, cb = (item >> 1) & 7, gb = item & 1;
         const int q = slice * LUT2_SLOTS + s;
         const int qq = q < p.n_slots ? q : 0;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
 
     uint4 codes[TPW][LUT2_SLOTS];
     auto load_tile = [&](int u) {
-        const int64_t it = t0 + wave + (int64_t)u * LUT_WAVES;
+        const int64_t it = t0 + wave + (int64_t)u * W;
         const uint32_t off = it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE;
 #pragma unroll
         for (int s = 0; s < LUT2_SLOTS; ++s) codes[u][s] = load_stream(slot_buf[s], slot_on[s] ? off : NO_TILE);
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
         const int trow_ = ((lane & 3) == 1 ? 8 : 0) + 4 * (oi_ >> 3) + ((oi_ >> 1) & 3);
 #pragma unroll
         for (int u = 0; u < TPW; ++u) {
-            const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow_;
+            const int64_t row = (t0 + wave + (int64_t)u * W) * TILE_ROWS + trow_;
             row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
         }
     }
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
 
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
-        const int item = wave + u * LUT_WAVES;
+        const int item = wave + u * W;
         const int s = item >> 4, cb = (item >> 1) & 7, gb = item & 1;
         floatx16_t t[2];
 #pragma unroll
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int64_t it = t0 + wave + (int64_t)u * LUT_WAVES;
+        const int64_t it = t0 + wave + (int64_t)u * W;
         if (it >= t1) break;                    // uniform across the wave
         floatx4_t d[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut2_kernel(Lut2Args p) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         if (!mine[u] || !fix_is_last(old_word[u], p.slices)) continue;
-        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow;
+        const int64_t row = (t0 + wave + (int64_t)u * W) * TILE_ROWS + trow;
         p.y[col * p.d_out + row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], p.slices));
         __hip_atomic_store(p.acc + col * p.d_out + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -248,6 +248,17 @@ hipError_t launch_gemv_lut2(const uint8_t* packed, const uint16_t* codebooks, co
     }
     a.tiles_per_block = tpb;
     const dim3 gd((unsigned)(a.slices * blocks)), bd(64 * LUT_WAVES);
+    // plans of at most 8 row tiles per workgroup run in 8-wave workgroups: the same tiles, sums and bits
+    // (4096x4096 k = 1: 4.56 -> 4.25 us; 1024 and 2048 rows 5-9 % faster at k = 1..4)
+    if (tpw == LUT_TILES_PER_WAVE && k <= 4 && tpb <= LUT_WAVES_SMALL) {
+        const dim3 bd8(64 * LUT_WAVES_SMALL);
+        constexpr int T = LUT_TILES_PER_WAVE, W8 = LUT_WAVES_SMALL;
+        if (k == 1) hipLaunchKernelGGL((gemv_lut2_kernel<1, T, W8>), gd, bd8, 0, s, a);
+        else if (k == 2) hipLaunchKernelGGL((gemv_lut2_kernel<2, T, W8>), gd, bd8, 0, s, a);
+        else if (k == 3) hipLaunchKernelGGL((gemv_lut2_kernel<3, T, W8>), gd, bd8, 0, s, a);
+        else hipLaunchKernelGGL((gemv_lut2_kernel<4, T, W8>), gd, bd8, 0, s, a);
+        return hipGetLastError();
+    }
     if (tpw == LUT_TILES_PER_WAVE_BIG) launch_lut2_k<LUT_TILES_PER_WAVE_BIG>(k, gd, bd, s, a);
     else launch_lut2_k<LUT_TILES_PER_WAVE>(k, gd, bd, s, a);
     return hipGetLastError();
