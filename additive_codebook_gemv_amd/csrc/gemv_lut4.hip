@@ -47,8 +47,8 @@ struct Lut4Args {
     int k, batch, n_slots, tiles_per_block;
 };
 
-template <int K, int TPW>
-__global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
+template <int K, int TPW, int W = LUT_WAVES>
+__global__ __launch_bounds__(64 * W) void gemv_lut4_kernel(Lut4Args p) {
     __shared__ __align__(16) uint8_t lds[CODEWORDS * 64 * LUT4_ENTRY];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -61,27 +61,34 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
     const __amdgpu_buffer_rsrc_t slot_buf =
         slot_rsrc(p.packed + (int64_t)plane * p.plane_bytes + (int64_t)gt * p.n_rt * TILE_BYTES, p.n_rt * TILE_BYTES);
 
-    // ---- table operands.  Wave w builds codewords 32*(w >> 1) .. +32 for groups 32*(w & 1) .. +32;
-    // its four products are the four columns.
-    const int cb = wave >> 1, gb = wave & 1;
+    // ---- table operands.  Item i (16 of them, 16 / W per wave: item wave + u * W) builds codewords
+    // 32*(i >> 1) .. +32 for groups 32*(i & 1) .. +32; its four products are the four columns.
+    constexpr int IW = 16 / W;
+    static_assert(IW * W == 16, "table items per wave");
     const int e0 = 4 * (lane >> 5);
-    const int64_t g = (int64_t)gt * TILE_GROUPS + gb * 32 + (lane & 31);
-    const bool gok = g < p.G;
-    const int64_t gc = gok ? g : p.G - 1;
-    const uint2 av = *reinterpret_cast<const uint2*>(p.codebooks + ((int64_t)plane * CODEWORDS + cb * 32 + (lane & 31)) *
-                                                                       GROUP + e0);
-    uint2 bv[LUT4_COLS];
+    uint2 av[IW], bv[IW][LUT4_COLS];
+    bool gok[IW];
 #pragma unroll
-    for (int c = 0; c < LUT4_COLS; ++c) {
-        const int cc = c < p.batch ? c : p.batch - 1;
-        bv[c] = *reinterpret_cast<const uint2*>(p.x + cc * p.d_in + gc * GROUP + e0);
+    for (int u = 0; u < IW; ++u) {
+        const int item = wave + u * W;
+        const int cb = item >> 1, gb = item & 1;
+        const int64_t g = (int64_t)gt * TILE_GROUPS + gb * 32 + (lane & 31);
+        gok[u] = g < p.G;
+        const int64_t gc = gok[u] ? g : p.G - 1;
+        av[u] = *reinterpret_cast<const uint2*>(p.codebooks + ((int64_t)plane * CODEWORDS + cb * 32 + (lane & 31)) *
+                                                                  GROUP + e0);
+#pragma unroll
+        for (int c = 0; c < LUT4_COLS; ++c) {
+            const int cc = c < p.batch ? c : p.batch - 1;
+            bv[u][c] = *reinterpret_cast<const uint2*>(p.x + cc * p.d_in + gc * GROUP + e0);
+        }
     }
     // operand loads of every wave go out before any code load (see the batch-1 kernel)
     __builtin_amdgcn_s_barrier();
 
     uint4 codes[TPW];
     auto load_tile = [&](int u) {
-        const int64_t it = t0 + wave + (int64_t)u * LUT_WAVES;
+        const int64_t it = t0 + wave + (int64_t)u * W;
         codes[u] = load_stream(slot_buf, it < t1 ? (uint32_t)(it * TILE_BYTES) + lane * TILE_ROWS : NO_TILE);
     };
     load_tile(0);
@@ -94,21 +101,26 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
     uint16_t row_scale[TPW];
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow;
+        const int64_t row = (t0 + wave + (int64_t)u * W) * TILE_ROWS + trow;
         row_scale[u] = p.scales[row < p.d_out ? row : p.d_out - 1];
     }
 #pragma unroll
-    for (int c = 0; c < LUT4_COLS; ++c)
-        if (!gok || c >= p.batch) bv[c] = make_uint2(0u, 0u);   // zero activation -> zero table entries
+    for (int u = 0; u < IW; ++u)
+#pragma unroll
+        for (int c = 0; c < LUT4_COLS; ++c)
+            if (!gok[u] || c >= p.batch) bv[u][c] = make_uint2(0u, 0u);   // zero activation -> zero entries
 
-    {
+#pragma unroll
+    for (int u = 0; u < IW; ++u) {
+        const int item = wave + u * W;
+        const int cb = item >> 1, gb = item & 1;
         floatx16_t t[LUT4_COLS];
 #pragma unroll
         for (int c = 0; c < LUT4_COLS; ++c) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) t[c][r] = 0.f;
-            t[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(half4_t, av),
-                                                        __builtin_bit_cast(half4_t, bv[c]), t[c], 0, 0, 0);
+            t[c] = __builtin_amdgcn_mfma_f32_32x32x8f16(__builtin_bit_cast(half4_t, av[u]),
+                                                        __builtin_bit_cast(half4_t, bv[u][c]), t[c], 0, 0, 0);
         }
         const int gl = gb * 32 + (lane & 31);
 #pragma unroll
@@ -139,7 +151,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
     }
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
-        const int64_t it = t0 + wave + (int64_t)u * LUT_WAVES;
+        const int64_t it = t0 + wave + (int64_t)u * W;
         if (it >= t1) break;                    // uniform across the wave
         floatx4_t d[4];
 #pragma unroll
@@ -179,7 +191,7 @@ __global__ __launch_bounds__(64 * LUT_WAVES) void gemv_lut4_kernel(Lut4Args p) {
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
         if (!mine[u] || !fix_is_last(old_word[u], p.n_slots)) continue;
-        const int64_t row = (t0 + wave + (int64_t)u * LUT_WAVES) * TILE_ROWS + trow;
+        const int64_t row = (t0 + wave + (int64_t)u * W) * TILE_ROWS + trow;
         p.y[col * p.d_out + row] = f2h(h2f(row_scale[u]) * (float)fix_total(old_word[u], term[u], p.n_slots));
         __hip_atomic_store(p.acc + col * p.d_out + row, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -228,6 +240,14 @@ hipError_t launch_gemv_lut4(const uint8_t* packed, const uint16_t* codebooks, co
     }
     a.tiles_per_block = tpb;
     const dim3 gd((unsigned)(a.n_slots * blocks)), bd(64 * LUT_WAVES);
+    // plans of at most 8 row tiles per workgroup run in 8-wave workgroups (two table items per wave): the
+    // same tiles, sums and bits (4096x4096 batch 4, k = 1: 5.25 -> 4.87 us; 1024 and 2048 rows 5-9 % faster)
+    if (tpw == LUT_TILES_PER_WAVE && tpb <= LUT_WAVES_SMALL) {
+        const dim3 bd8(64 * LUT_WAVES_SMALL);
+        if (k == 1) hipLaunchKernelGGL((gemv_lut4_kernel<1, LUT_TILES_PER_WAVE, LUT_WAVES_SMALL>), gd, bd8, 0, s, a);
+        else hipLaunchKernelGGL((gemv_lut4_kernel<2, LUT_TILES_PER_WAVE, LUT_WAVES_SMALL>), gd, bd8, 0, s, a);
+        return hipGetLastError();
+    }
     if (tpw == LUT_TILES_PER_WAVE_BIG) launch_lut4_k<LUT_TILES_PER_WAVE_BIG>(k, gd, bd, s, a);
     else launch_lut4_k<LUT_TILES_PER_WAVE>(k, gd, bd, s, a);
     return hipGetLastError();
