@@ -180,8 +180,9 @@ def aqd_gemv(packed: torch.Tensor, codebooks: torch.Tensor, scales: torch.Tensor
     L = layer(d_out, d_in, M)
     if out is None:
         out = torch.empty((batch, d_out), dtype=torch.float16, device=x_rot.device)
-    need = int(lib().aqd_gemv_workspace_bytes(ctypes.byref(L), batch))
-    if need and workspace is None:
+    # only a missing workspace is sized here; the library checks the size of a given one
+    need = int(lib().aqd_gemv_workspace_bytes(ctypes.byref(L), batch)) if workspace is None else 0
+    if need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
     _check(lib().aqd_gemv(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x2), _ptr(out), batch,
                           ctypes.byref(L), _ptr(workspace), workspace.numel() if workspace is not None else 0,
@@ -238,8 +239,9 @@ def aqd_gemv_grouped(linears, k: int, x_rot: torch.Tensor, d_in: int,
         outs.append(y)
         parts.append((packed, codebooks, scales, y, d_out, M))
     arr = _linears(parts)
-    need = int(lib().aqd_gemv_grouped_workspace_bytes(arr, len(parts), d_in))
-    if need and workspace is None:
+    # only a missing workspace is sized here; the library checks the size of a given one
+    need = int(lib().aqd_gemv_grouped_workspace_bytes(arr, len(parts), d_in)) if workspace is None else 0
+    if need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
     nws = workspace.numel() if workspace is not None else 0
     if signs is not None:
@@ -282,8 +284,9 @@ def aqd_gemm_small_batch(packed: torch.Tensor, codebooks: torch.Tensor, scales: 
     L = layer(d_out, d_in, M)
     if out is None:
         out = torch.empty((batch, d_out), dtype=torch.float32, device=x_rot.device)
-    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch))
-    if need and workspace is None:
+    # only a missing workspace is sized here; the library checks the size of a given one
+    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch)) if workspace is None else 0
+    if need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
     _check(lib().aqd_gemm_small_batch(_ptr(packed), _ptr(codebooks), _ptr(scales), k, _ptr(x_rot), x_dtype,
                                       _ptr(out), batch, ctypes.byref(L), _ptr(workspace),
@@ -338,8 +341,9 @@ def aqd_gemm_small_batch_tiered(packed: torch.Tensor, codebooks: torch.Tensor, s
     L = layer(d_out, d_in, M)
     if out is None:
         out = torch.empty((batch, d_out), dtype=torch.float32, device=x_rot.device)
-    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch))
-    if need and workspace is None:
+    # only a missing workspace is sized here; the library checks the size of a given one
+    need = int(lib().aqd_gemm_small_batch_workspace_bytes(ctypes.byref(L), batch)) if workspace is None else 0
+    if need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=x_rot.device)
     karr = (ctypes.c_int32 * batch)(*[int(k) for k in ks])
     _check(lib().aqd_gemm_small_batch_tiered(_ptr(packed), _ptr(codebooks), _ptr(scales), karr, _ptr(x_rot),
