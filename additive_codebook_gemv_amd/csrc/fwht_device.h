@@ -105,4 +105,62 @@ __device__ __forceinline__ void fwht_block(float (&v)[B / 64], int lane) {
     for (int e = 0; e < E; ++e) v[e] *= sc;
 }
 
+// The same network on 256 consecutive inputs laid out as the B operand of a
+// 32x32x8 matrix product over 32 groups of 8: lane l holds the four inputs
+// 8 (l mod 32) + 4 (l / 32) + r, r = 0..3, so index bits 0-1 are the register
+// r, bit 2 is lane bit 5 and bits 3-7 are lane bits 0-4.  A block of B inputs
+// (64, 128 or 256; blocks start at multiples of B) takes the stages 1 .. B/2
+// apart in the order fwht_block takes them, each element becoming the same
+// lower + upper or lower - upper of the same two values, so every output has
+// the bits fwht_block gives it.
+template <int B>
+__device__ __forceinline__ void fwht_operand(float (&v)[4], int lane) {
+    using namespace fwht_detail;
+    static_assert(B == 64 || B == 128 || B == 256, "block");
+    // distances 1 and 2: register pairs (r, r ^ 1), then (r, r ^ 2)
+#pragma unroll
+    for (int hb = 1; hb <= 2; hb <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if ((r & hb) == 0) {
+                const float a = v[r], c = v[r | hb];
+                v[r] = a + c;
+                v[r | hb] = a - c;
+            }
+        }
+    }
+    // distance 4: the two 32-lane halves; lanes 0-31: (own, lane + 32), lanes 32-63: (lane - 32, own)
+    const float s32 = (lane & 32) ? -1.f : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
+        v[r] = __builtin_fmaf(s32, __uint_as_float(q[1]), __uint_as_float(q[0]));
+    }
+    // distances 8, 16, 32 (and 64, 128 for the larger blocks): lanes 1, 2, 4 (8, 16) apart
+    const float s1 = (lane & 1) ? -1.f : 1.f, s2 = (lane & 2) ? -1.f : 1.f, s4 = (lane & 4) ? -1.f : 1.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaf(s1, v[r], partner<1>(v[r]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaf(s2, v[r], partner<2>(v[r]));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaf(s4, v[r], partner<4>(v[r]));
+    if constexpr (B >= 128) {
+        const float s8 = (lane & 8) ? -1.f : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = __builtin_fmaf(s8, v[r], partner<8>(v[r]));
+    }
+    if constexpr (B == 256) {
+        // even 16-lane rows: (own, lane + 16); odd rows: (lane - 16, own)
+        const float s16 = (lane & 16) ? -1.f : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[r]), __float_as_uint(v[r]), false, false);
+            v[r] = __builtin_fmaf(s16, __uint_as_float(q[1]), __uint_as_float(q[0]));
+        }
+    }
+    const float sc = inv_sqrt_block<B>();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] *= sc;
+}
+
 }  // namespace aqd

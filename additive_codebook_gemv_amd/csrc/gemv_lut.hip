@@ -80,7 +80,9 @@ struct LutArgs {
 // HB > 0: x is the raw fp16 activation and the workgroup applies the block
 // Walsh-Hadamard rotation (block HB) to the inputs its tables need, with the
 // butterflies and rounding of the standalone rotation (same bits), after the
-// optional sign flips of the randomized variant.
+// optional sign flips of the randomized variant: with four slots on one group
+// tile every wave rotates its own activation fragment in registers, otherwise
+// a few waves rotate each distinct block once and share it through LDS.
 //
 // S is the number of slots a workgroup holds tables for (1, 2 or 4): 64 KiB of
 // LDS per pair of slots (S = 1 uses half of one pair's entries).  Building a
@@ -103,9 +105,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     static_assert(S == 1 || S == 2 || S == 4, "slots per workgroup");
     constexpr int NPAIR = S >= 2 ? S / 2 : 1;                      // 64 KiB table regions
     constexpr int H = S >= 2 ? 2 : 1;                              // slots per region
-    constexpr int XS_BYTES = HB > 0 ? S * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
+    // When K is a multiple of S every slot of the slice lies in one group tile.
+    constexpr bool ONE_TILE = K % S == 0;
+    // The rotating launch rotates in registers (each wave its own activation fragments) where four
+    // slots share one group tile; elsewhere the distinct blocks are rotated once, by as many waves,
+    // and shared through LDS.  Both give the bits of the standalone rotation.
+    constexpr bool REG_ROT = HB > 0 && S == 4 && ONE_TILE;
+    constexpr bool LDS_ROT = HB > 0 && !REG_ROT;
+    constexpr int XS_SLOTS = ONE_TILE ? 1 : S;                     // staged slots (distinct group tiles)
+    constexpr int XS_BYTES = LDS_ROT ? XS_SLOTS * TILE_GROUPS * GROUP * 2 : 0;   // rotated inputs, fp16
     __shared__ __align__(16) uint8_t lds[NPAIR * LUT_PAIR_BYTES + XS_BYTES + 16];
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + NPAIR * LUT_PAIR_BYTES);   // [slot][512]
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + NPAIR * LUT_PAIR_BYTES);   // [staged slot][512]
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -148,6 +158,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
     constexpr int ITEMS = 16 * NPAIR / WAVES;
     static_assert(ITEMS * WAVES == 16 * NPAIR, "items per wave");
     uint2 av[ITEMS][H], bv[ITEMS][H];
+    uint64_t sw[ITEMS][H] = {};                                  // sign words (rotation in registers)
     bool bok[ITEMS][H];
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
@@ -163,24 +174,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
             bok[u][h] = q < n_slots && g < G;
             const int64_t gc = g < G ? g : G - 1;
             av[u][h] = *reinterpret_cast<const uint2*>(codebooks + ((int64_t)(qq % K) * CODEWORDS + c) * GROUP + e0);
-            // when K is a multiple of S every slot of the slice lies in one group tile, and the
-            // items of a wave share gb: one activation fragment serves them all
-            constexpr bool ONE_TILE = K % S == 0;
-            if (HB == 0) {
-                if (!ONE_TILE || (u == 0 && h == 0)) bv[u][h] = *reinterpret_cast<const uint2*>(xin + gc * GROUP + e0);
-                else bv[u][h] = bv[0][0];
+            // The activation fragment (raw when rotated in registers, below; read from LDS when the
+            // rotation is staged there).  With one group tile the items of a wave share gb: one
+            // fragment serves them all.
+            if constexpr (!LDS_ROT) {
+                if (!ONE_TILE || (u == 0 && h == 0)) {
+                    bv[u][h] = *reinterpret_cast<const uint2*>(xin + gc * GROUP + e0);
+                    // randomized rotation: the sign bits of the fragment's four inputs, bit n % 64 of word n / 64
+                    if (REG_ROT && p.signs) sw[u][h] = p.signs[(gc * GROUP + e0) / 64];
+                } else {
+                    bv[u][h] = bv[0][0];
+                    if (REG_ROT && p.signs) sw[u][h] = sw[0][0];
+                }
             }
         }
     }
-    // raw activation blocks for the rotation: slot s needs inputs 512*tile .. +512 (tile = q / K),
-    // i.e. 512 / HB blocks; wave w takes blocks w, w + WAVES, ...
-    constexpr int BLK_PER_SLOT = HB > 0 ? TILE_GROUPS * GROUP / HB : 1;
-    constexpr int NBLK = S * BLK_PER_SLOT;
+    // raw activation blocks of the staged rotation: staged slot s needs inputs 512*tile .. +512
+    // (tile = q / K), i.e. 512 / HB blocks; wave w takes blocks w, w + WAVES, ...
+    constexpr int BLK_PER_SLOT = LDS_ROT ? TILE_GROUPS * GROUP / HB : 1;
+    constexpr int NBLK = XS_SLOTS * BLK_PER_SLOT;
     constexpr int BPW = (NBLK + WAVES - 1) / WAVES;
-    constexpr int E = HB > 0 ? HB / 64 : 1;
+    constexpr int E = LDS_ROT ? HB / 64 : 1;
     float xv[BPW][E];
     bool xok[BPW];
-    if (HB > 0) {
+    if constexpr (LDS_ROT) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
             const int blk = wave + b * WAVES;
@@ -222,9 +239,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
 #pragma unroll
         for (int h = 0; h < H; ++h) {
             asm volatile("" ::"v"(av[u][h].x), "v"(av[u][h].y) : "memory");
-            if (HB == 0) asm volatile("" ::"v"(bv[u][h].x), "v"(bv[u][h].y) : "memory");
+            if (!LDS_ROT) asm volatile("" ::"v"(bv[u][h].x), "v"(bv[u][h].y) : "memory");
         }
-    if (HB > 0) {
+    if constexpr (LDS_ROT) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b)
 #pragma unroll
@@ -245,25 +262,52 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lut_kernel(const uint8_t* __r
         for (int s = 0; s < S; ++s) load_slot(u, s);
     };
     load_tile(0);
-    if (HB > 0) {
+    if constexpr (LDS_ROT) {
 #pragma unroll
         for (int b = 0; b < BPW; ++b) {
             const int blk = wave + b * WAVES;
             if (blk >= NBLK) continue;                          // uniform over the wave
-            if constexpr (HB > 0) fwht_block<HB>(xv[b], lane);
+            fwht_block<HB>(xv[b], lane);
 #pragma unroll
             for (int e = 0; e < E; ++e) xs[blk * HB + e * 64 + lane] = xok[b] ? f2h(xv[b][e]) : (uint16_t)0;
         }
-        __syncthreads();                                        // rotated inputs of every slot are in LDS
+        __syncthreads();                                        // rotated inputs of every staged slot are in LDS
 #pragma unroll
         for (int u = 0; u < ITEMS; ++u) {
             const int item = wave + u * WAVES;
             const int gb = item & 1, pair = item >> 4;
 #pragma unroll
             for (int h = 0; h < H; ++h)
-                bv[u][h] = *reinterpret_cast<const uint2*>(xs + (2 * pair + h) * (TILE_GROUPS * GROUP) +
+                bv[u][h] = *reinterpret_cast<const uint2*>(xs + (ONE_TILE ? 0 : 2 * pair + h) * (TILE_GROUPS * GROUP) +
                                                            (gb * 32 + (lane & 31)) * GROUP + 4 * (lane >> 5));
         }
+    }
+    if constexpr (REG_ROT) {
+        // Each wave rotates the fragment it holds, in registers: a fragment is 256 inputs starting at a
+        // multiple of 256, so it holds whole blocks, and fwht_operand gives them the bits of the
+        // standalone rotation.  Fragments past the input are rotated from clamped inputs and then
+        // zeroed with their groups (below); a block never straddles the end, d_in being a multiple of HB.
+        const int pos = 8 * (lane & 7) + 4 * (lane >> 5);      // bit of the fragment's first input in its word
+#pragma unroll
+        for (int u = 0; u < ITEMS; ++u)
+#pragma unroll
+            for (int h = 0; h < H; ++h) {
+                if (ONE_TILE && (u != 0 || h != 0)) {
+                    bv[u][h] = bv[0][0];
+                    continue;
+                }
+                const uint2 raw = bv[u][h];
+                float v[4] = {h2f((uint16_t)(raw.x & 0xFFFF)), h2f((uint16_t)(raw.x >> 16)),
+                              h2f((uint16_t)(raw.y & 0xFFFF)), h2f((uint16_t)(raw.y >> 16))};
+                if (p.signs) {                                  // eps = -1 where the bit is set
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if ((sw[u][h] >> (pos + r)) & 1ull) v[r] = -v[r];
+                }
+                fwht_operand<(HB > 0 ? HB : 64)>(v, lane);
+                bv[u][h] = make_uint2((uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16),
+                                      (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16));
+            }
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u)
