@@ -40,8 +40,8 @@ CONFIG_ID = 3            # the MLP workload family (gate/up/down 14336 x 4096 an
 
 # HBM bytes per k=4 launch from rocprofv3 FETCH_SIZE + WRITE_SIZE (each scaled by a 64 MiB copy), valid
 # only for the kernel sources they were taken on: the summary under profiles/ gives the commands.
-TRAFFIC_K4_BYTES = 30673913
-TRAFFIC_K4_SOURCE_SHA256_PREFIX = "7500c52a6a8f8d39"
+TRAFFIC_K4_BYTES = 30674934
+TRAFFIC_K4_SOURCE_SHA256_PREFIX = "4f14952b0c17a702"
 TIMING_ROUNDS = 4          # rounds the timed steps are split into (see main)
 # the batch-1 GEMV kernel's source and the headers it includes
 HEADLINE_SOURCES = ("gemv_lut.hip", "lut_device.h", "fixed_sum.h", "fwht_device.h", "aqd_internal.h")
