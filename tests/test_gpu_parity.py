@@ -528,6 +528,9 @@ def test_rotate_gemv_grouped_matches_rotate_then_gemv(orc, shapes, d_in, block, 
     ([4096, 1024, 1024], 4096, 128, 4),     # q, k, v
     ([4096], 14336, 256, 2),                 # down projection
     ([300, 17], 576, 64, 3),                 # ragged rows, a partial group tile
+    ([14336, 14336], 4096, 128, 4),          # gate, up: four slots on one group tile, rotated in registers
+    ([4096], 14336, 256, 4),                 # down, rotated in registers
+    ([8200], 4224, 128, 4),                  # in registers with ragged rows and a half-empty last group tile
 ])
 def test_rotate_gemv_grouped_signed(orc, shapes, d_in, block, k):
     """Randomized rotation inside the launch: the bits of the signed standalone rotation followed by the

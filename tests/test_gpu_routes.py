@@ -175,6 +175,7 @@ def test_stack_fused_schedule_sampled(orc):
     ([14336, 14336], 4096, 128),           # gate, up
     ([4096], 14336, 256),                  # down
     ([14336, 1024], 4096, 128),            # members that take 4 and 2 table slots at k = 3, 4: two launches
+    ([8200], 4224, 128),                   # ragged rows, last group tile half past the input (k = 4: in registers)
 ])
 def test_rotating_launch_every_stack_shape_and_k(orc, shapes, d_in, block, k):
     g = wl.rng(621, extra=d_in + block + sum(shapes) + k)
