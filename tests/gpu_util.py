@@ -7,7 +7,6 @@ import os
 import numpy as np
 import torch
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TOL = 2e-3   # max normwise relative error against the fp64 oracle
 
 _records = []
@@ -43,14 +42,15 @@ def rms_rel(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 def record(**kw):
-    """Keep a parity figure; written to gpurun_out/parity_report.jsonl at the end of the session."""
+    """Keep a parity figure (test, case, error); appended at the end of the session, one JSON object per
+    line, to the file that the environment variable AQD_PARITY_REPORT names, if it names one."""
     _records.append(kw)
 
 
 def flush_records():
-    out = os.path.join(ROOT, "gpurun_out")
-    if _records and os.path.isdir(out):
-        with open(os.path.join(out, "parity_report.jsonl"), "a") as f:
+    path = os.environ.get("AQD_PARITY_REPORT")
+    if _records and path and os.path.isdir(os.path.dirname(os.path.abspath(path))):
+        with open(path, "a") as f:
             for r in _records:
                 f.write(json.dumps(r) + "\n")
     _records.clear()
